@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of the ZeRO-1 mixed-precision Adam step on one MI355X.
+
+One step = the whole hot path on the shard: norm/overflow pass, finalize, fused
+unscale + clip + AdamW + cast update.  Inputs are synthetic and already resident in
+HBM.  Prints one JSON line:
+  value     params/s over the timed steps (wall clock between synchronizations)
+  roofline  the update kernel (the dominant one): algorithmic bytes per launch over its
+            average duration from HIP events on its stream, against 8 TB/s
+  cpu_baseline  the CPU oracle, single thread, on a bounded sample of the workload
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+UPDATE_BYTES_PER_PARAM = 28      # grad 2 + master/m/v 12 read; master/m/v 12 + half 2 written
+STEP_BYTES_PER_PARAM = 30        # + the norm pass's 2-byte gradient read
+KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "zero1_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "update_kernel_neox20b_shard_215m_pmc.txt")
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(workload, n):
+    """HBM bytes per update launch from the committed rocprofv3 PMC summary, scaled by
+    its copy-kernel calibration factor; None if absent or taken on other kernel code."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    try:
+        if vals.get("kernel_source_sha256") != kernel_sha() or vals.get("workload") != workload:
+            return None
+        kib = float(vals["fetch_kib_per_dispatch"]) + float(vals["write_kib_per_dispatch"])
+        return kib * 1024.0 * float(vals["copy_factor"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
+    """The oracle as it stands, one thread, on the first `sample` params of the shard."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import oracle as O
+
+    sample = min(sample, w.numel)
+    segs, left = [], sample
+    for n, d in w.segments:
+        if left == 0:
+            break
+        segs.append((min(n, left), d))
+        left -= segs[-1][0]
+    st0 = W.host_init(w, n=sample)
+    h = w.hyper
+    cfg = O.Config(beta1=h.beta1, beta2=h.beta2, eps=h.eps, weight_decay=h.weight_decay,
+                   clip_norm=h.clip_norm, predivide_factor=h.predivide_factor,
+                   dp_world_size=h.dp_world_size, dtype=h.dtype, scaler_mode=h.scaler_mode,
+                   growth_interval=h.growth_interval, growth_factor=h.growth_factor,
+                   backoff_factor=h.backoff_factor, min_scale=h.min_scale)
+    st = O.Scaler(loss_scale=h.init_scale)
+    spent, steps = 0.0, 0
+    while spent < budget_s and steps < 50:
+        g = W.host_grads(w, steps, st.loss_scale, n=sample)
+        osegs, off = [], 0
+        for n, d in segs:
+            sl = slice(off, off + n)
+            osegs.append(dict(grad=g[sl], half=st0["half"][sl], master=st0["master"][sl],
+                              m=st0["m"][sl], v=st0["v"][sl], decay=d))
+            off += n
+        t0 = time.perf_counter()
+        O.step(cfg, st, np.float32(h.lr), osegs)
+        spent += time.perf_counter() - t0
+        steps += 1
+    return {"value": sample * steps / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sample} params of the shard ({len(segs)} segments), {steps} steps, "
+                      f"{spent:.1f} s of single-thread oracle time (fp64 scalar C, -O2)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="neox20b_shard_215m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing-events", action="store_true",
+                    help="time whole steps only (no per-kernel events)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the step is per-rank work and multi-GPU runs are not part of it", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixed_precision_zero_amd as Z
+    import workloads as W
+
+    if args.workload not in W.BENCH_WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; one of {sorted(W.BENCH_WORKLOADS)}")
+    w = W.BENCH_WORKLOADS[args.workload]()
+    n = w.numel
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    dt = torch.float16 if w.hyper.dtype == W.F16 else torch.bfloat16
+    print(f"[bench] workload {w.name}: {n} params, {len(w.segments)} segments, "
+          f"{'flat' if w.flat else 'separate allocations'}", file=sys.stderr, flush=True)
+
+    keep = []
+    segs = []
+    if w.flat:
+        bufs = {k: torch.empty(n, dtype=t, device=dev) for k, t in
+                (("grad", dt), ("half", dt), ("master", torch.float32), ("m", torch.float32),
+                 ("v", torch.float32))}
+        W.device_init_(w, bufs["master"], bufs["half"], bufs["m"], bufs["v"])
+        W.device_grads_(w, bufs["grad"], 0, w.hyper.init_scale)
+        off = 0
+        for numel, decay in w.segments:
+            sl = slice(off, off + numel)
+            segs.append(Z.segment(*(bufs[k][sl] for k in ("grad", "half", "master", "m", "v")),
+                                  decay))
+            off += numel
+        keep.append(bufs)
+    else:
+        off = 0
+        for i, (numel, decay) in enumerate(w.segments):
+            a = {k: torch.empty(numel, dtype=t, device=dev) for k, t in
+                 (("grad", dt), ("half", dt), ("master", torch.float32), ("m", torch.float32),
+                  ("v", torch.float32))}
+            W.device_init_(w, a["master"], a["half"], a["m"], a["v"], i + 1)
+            W.device_grads_(w, a["grad"], 0, w.hyper.init_scale, off)
+            segs.append(Z.segment(a["grad"], a["half"], a["master"], a["m"], a["v"], decay))
+            keep.append(a)
+            off += numel
+    stream = torch.cuda.current_stream()
+    h = Z.neox_zero1_create(Z.neox_zero1_default_config(
+        beta1=w.hyper.beta1, beta2=w.hyper.beta2, eps=w.hyper.eps,
+        weight_decay=w.hyper.weight_decay, clip_norm=w.hyper.clip_norm,
+        predivide_factor=w.hyper.predivide_factor, dp_world_size=w.hyper.dp_world_size,
+        dtype=w.hyper.dtype, scaler_mode=w.hyper.scaler_mode,
+        growth_interval=w.hyper.growth_interval, init_scale=w.hyper.init_scale,
+        min_scale=w.hyper.min_scale), segs, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+
+    timed_events = not args.no_timing_events
+    if timed_events:
+        Z.neox_zero1_timing_begin(h, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st = Z.neox_scaler_state(h)
+    kernel_ms = None
+    if timed_events:
+        sums, k = Z.neox_zero1_timing_end(h)
+        kernel_ms = [s / k for s in sums]
+    Z.neox_zero1_destroy(h)
+    assert st.skipped_total == 0 and st.step == args.warmup + args.steps, "bench steps were skipped"
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = n / (ms_per_step * 1e-3)
+    out = {
+        "metric": "params/sec per fused ZeRO-1 Adam step; achieved HBM GB/s vs MI355X peak",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "params": n, "segments": len(w.segments),
+                   "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
+                   "layout": "flat shard" if w.flat else "separate allocations"},
+        "hbm": {"step_bytes": STEP_BYTES_PER_PARAM * n,
+                "step_gbps": STEP_BYTES_PER_PARAM * n / (ms_per_step * 1e-3) / 1e9,
+                "step_frac_of_peak": STEP_BYTES_PER_PARAM * n / (ms_per_step * 1e-3) / 1e9
+                / HBM_PEAK_GBS},
+    }
+    if kernel_ms:
+        upd_gbs = UPDATE_BYTES_PER_PARAM * n / (kernel_ms[2] * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": upd_gbs / HBM_PEAK_GBS,
+                           "traffic": read_traffic(w.name, n),
+                           "kernel": "update_kernel", "avg_ms": kernel_ms[2],
+                           "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n}
+        out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],
+                                "update": kernel_ms[2]}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle, one thread)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * neox_zero1.h -- C ABI of the MI355X (gfx950) ZeRO-1 mixed-precision Adam step.
+ *
+ * One call runs the optimizer step that one data-parallel rank performs on its own
+ * flat shard after the gradients have been reduced: FP32 Adam moments and FP32
+ * master weights, FP16 or BF16 gradients and model copy, dynamic loss scaling that
+ * skips the step on an inf/NaN gradient, a gradient pre-divide factor, clipping by
+ * the global L2 norm, decoupled weight decay, and the write-back of the half copy.
+ *
+ * Sources (web pages on GPT-NeoX and OPT training):
+ *   [NeoX] "GPT-NeoX: how it opened the door to democratised 100B-scale training"
+ *          (ainews.cool article), section 技术深度解析 (technical deep dive): with
+ *          ZeRO stage 1 the Adam moments are split over the data-parallel GPUs and
+ *          each device updates only the shard it owns; parallelism-strategy table:
+ *          DP + ZeRO communicates by reduce-scatter / all-gather.
+ *   [OPT]  "OPT: Open Pre-trained Transformer Language Models" (paper card),
+ *          section 计算设置 (compute setup): Adam state in FP32, sharded; FP16
+ *          weights; dynamic loss scaling.  Section 瓶颈 (bottlenecks): about 16
+ *          bytes of model state per parameter; loss-scale collapse accompanies
+ *          divergence.  Section 方法适配 (method adaptation): gradient pre-divide
+ *          factor; clipping changed from 1.0 to 0.3; scaler reset / restart.
+ * The pages give no formulas.  The step computes Adam with bias correction (Kingma &
+ * Ba 2015), decoupled weight decay (Loshchilov & Hutter), loss scaling with skip /
+ * back-off / growth (Micikevicius et al. 2018) and clipping by min(1, c / ||g||).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers (e.g. torch tensors' data_ptr()
+ *     on a ROCm build); everything else is host memory.
+ *   - hip_stream is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Return value: NEOX_OK (0) or a negative NEOX_E* code.  Nothing throws or aborts
+ *     across the ABI.  Arguments are validated before any work is enqueued; on error
+ *     nothing is enqueued and neox_zero1_last_error() describes the failure.
+ *   - A handle may be used by one host thread at a time.
+ */
+#ifndef NEOX_ZERO1_H
+#define NEOX_ZERO1_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NEOX_OK       0
+#define NEOX_EINVAL  (-1)   /* bad argument: null, misaligned, zero size, out of range */
+#define NEOX_EHIP    (-2)   /* a HIP runtime call failed                               */
+#define NEOX_ENOMEM  (-3)   /* device or host allocation failed                        */
+
+#define NEOX_F16  1         /* IEEE-754 binary16 gradients and model copy */
+#define NEOX_BF16 2         /* bfloat16 gradients and model copy          */
+
+#define NEOX_SCALER_DYNAMIC 0   /* back off on overflow, grow after clean runs */
+#define NEOX_SCALER_STATIC  1   /* fixed scale; overflow still skips the step  */
+
+#define NEOX_SEG_DECAY 1u       /* segment receives decoupled weight decay      */
+#define NEOX_PAD_TENSOR 0xFFFFFFFFu
+
+/* Create-time configuration.  neox_zero1_default_config() fills the values the
+ * OPT-style recipe uses (betas 0.9 / 0.95, eps 1e-8, decay 0.01, clip 1.0, f = D = 1,
+ * fp16, dynamic scaler starting at 2^16, x0.5 on overflow, x2 after 1000 clean steps,
+ * floor 1.0). */
+typedef struct neox_zero1_config {
+    double  beta1, beta2;          /* in [0, 1)                                         */
+    double  eps;                   /* >= 0, added to sqrt(v_hat)                        */
+    double  weight_decay;          /* >= 0, decoupled: w -= lr * wd * w (DECAY segments) */
+    double  clip_norm;             /* > 0: clip to this global L2 norm; <= 0: no clip   */
+    double  predivide_factor;      /* f > 0: each rank divided its gradient by f        */
+    int32_t dp_world_size;         /* D >= 1: ranks whose gradients were summed         */
+    int32_t dtype;                 /* NEOX_F16 or NEOX_BF16 (gradients and half copy)   */
+    int32_t scaler_mode;           /* NEOX_SCALER_DYNAMIC or NEOX_SCALER_STATIC         */
+    int32_t growth_interval;       /* >= 1 clean steps between growths                  */
+    double  init_scale;            /* > 0, finite in FP32: scale of the first step       */
+    double  growth_factor;         /* >= 1                                              */
+    double  backoff_factor;        /* in (0, 1]                                         */
+    double  min_scale;             /* > 0: floor of the dynamic scale                   */
+    /* Resume: state of a previous run as read by neox_scaler_state(). */
+    int64_t init_step;             /* applied steps so far (t), >= 0                    */
+    int64_t init_skipped;          /* skipped steps so far, >= 0                        */
+    int32_t init_good_steps;       /* clean steps since the last growth / overflow      */
+    int32_t init_consecutive_overflows;
+    /* Launch shape; 0 selects the default.  Results other than the norm's last bits
+     * do not depend on either. */
+    uint32_t chunk_elems;          /* elements per work chunk: multiple of 8, 256..2^24 */
+    uint32_t norm_blocks;          /* blocks of the norm pass                           */
+} neox_zero1_config;
+
+/* One contiguous run of parameters of the shard, with its five device arrays, each
+ * holding numel elements:
+ *   grad        device, read-only: gradient in `dtype`, already summed over the D
+ *               ranks after each rank divided by f, still multiplied by the loss scale
+ *               of the step it is used in.  2-byte aligned.
+ *   half        device, written on applied steps: model copy in `dtype`.  2-byte aligned.
+ *   master      device FP32 master weights.           4-byte aligned.
+ *   exp_avg     device FP32 first moment m.           4-byte aligned.
+ *   exp_avg_sq  device FP32 second moment v.          4-byte aligned.
+ * 16-byte alignment of all five (at the same element) is the fast path; any other
+ * alignment is handled.  Segments must not overlap one another.  flags: NEOX_SEG_DECAY.
+ * tensor_id and tensor_offset are informational (as produced by neox_zero1_partition). */
+typedef struct neox_segment {
+    const void* grad;
+    void*       half;
+    float*      master;
+    float*      exp_avg;
+    float*      exp_avg_sq;
+    uint64_t    numel;
+    uint32_t    flags;
+    uint32_t    tensor_id;
+    uint64_t    tensor_offset;
+} neox_segment;
+
+/* Scaler / step state after the last enqueued step. */
+typedef struct neox_scaler_state_t {
+    float    loss_scale;           /* scale the next step's gradient must carry          */
+    int32_t  good_steps;           /* clean steps since the last growth or overflow      */
+    int64_t  step;                 /* applied steps (t)                                  */
+    int64_t  skipped_total;        /* skipped steps                                      */
+    int32_t  consecutive_overflows;/* overflows in a row; a climbing count at the scale
+                                      floor is the loss-scale collapse [OPT, 瓶颈]       */
+    int32_t  last_skipped;         /* 1 if the last step was skipped                     */
+    float    last_grad_norm;       /* global L2 norm of the unscaled gradient; +inf on a
+                                      skipped step                                       */
+    float    last_clip_coef;       /* applied clip coefficient (1 when not clipped)      */
+    double   last_sumsq;           /* squared norm in double (0 on a skipped step)       */
+    const float* device_loss_scale;/* device address of loss_scale, for scaling the next
+                                      loss on the device without a host sync             */
+} neox_scaler_state_t;
+
+/* Segment of a rank's shard as produced by neox_zero1_partition(). */
+typedef struct neox_shard_segment {
+    uint64_t shard_offset;         /* first element within the rank's flat shard         */
+    uint64_t numel;
+    uint64_t tensor_offset;        /* first element within the tensor                    */
+    uint32_t tensor_id;            /* index into the tensor list; NEOX_PAD_TENSOR for the
+                                      zero padding at the end of the flat concat          */
+    uint32_t flags;                /* NEOX_SEG_DECAY if the tensor decays                */
+} neox_shard_segment;
+
+typedef struct neox_zero1 neox_zero1;
+
+/* Fill *cfg with the defaults listed above.  Host only. */
+int neox_zero1_default_config(neox_zero1_config* cfg);
+
+/* ZeRO-1 shard layout [NeoX, 技术深度解析 and its parallelism table]: the tensors
+ * (host arrays tensor_numel[ntensors], tensor_decay[ntensors] with 0 / 1) are
+ * concatenated in order, the total is padded with zero elements to a multiple of
+ * dp_world_size * align, and rank `rank` owns elements [rank*P, (rank+1)*P) with
+ * P = padded / dp_world_size.  Writes up to `cap` segments (the intersections of each
+ * tensor, then the padding, with that range, in order) to the host array `out`, the
+ * number of segments to *nseg_out and P to *shard_numel_out.  Call with cap = 0 to size
+ * `out`.  Host only; never touches the GPU.
+ * Errors: NEOX_EINVAL for null outputs, dp_world_size or align of 0, rank out of range,
+ * a null input with ntensors > 0, or a 64-bit overflow of the total. */
+int neox_zero1_partition(const uint64_t* tensor_numel, const uint8_t* tensor_decay,
+                         uint64_t ntensors, uint32_t dp_world_size, uint32_t rank,
+                         uint32_t align, neox_shard_segment* out, uint64_t cap,
+                         uint64_t* nseg_out, uint64_t* shard_numel_out);
+
+/* Create a step handle for one shard.  cfg and segs[nseg] are host memory, copied
+ * (the caller may free them on return).  The caller keeps ownership of every device
+ * array; they must stay valid, and not be written by anyone else while a step runs,
+ * until neox_zero1_destroy().  The library allocates its own device scratch (work
+ * table, per-block partial sums, a state block) and uploads it on hip_stream, then
+ * synchronizes that stream.  *out receives the handle.
+ * Errors: NEOX_EINVAL (null pointers, nseg == 0, a zero-length or misaligned segment,
+ * a config field out of the ranges above), NEOX_ENOMEM, NEOX_EHIP. */
+int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg,
+                      void* hip_stream, neox_zero1** out);
+
+/* Enqueue one step on hip_stream and return without waiting: a norm/overflow pass
+ * over every gradient, a one-block finalize (skip decision, clip coefficient, step
+ * count, bias corrections, loss-scale update, all on the device), and the fused
+ * unscale + clip + AdamW + cast update, which returns at once when the finalize
+ * decided to skip.  The gradient must be complete in stream order before this call.
+ * On a skipped step master, exp_avg, exp_avg_sq and half are not written.
+ * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
+int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream);
+
+/* Wait for the last enqueued step (its stream) and copy the state to *out.
+ * Errors: NEOX_EINVAL (null), NEOX_EHIP. */
+int neox_scaler_state(neox_zero1* h, neox_scaler_state_t* out);
+
+/* Wait for outstanding work and free the library's scratch (never caller memory).
+ * NULL is a no-op returning NEOX_OK. */
+int neox_zero1_destroy(neox_zero1* h);
+
+/* Per-kernel timing for profiling.  neox_zero1_timing_begin(h, max_steps) makes the
+ * next max_steps steps record HIP events around each of the three kernels on their
+ * stream; neox_zero1_timing_end() waits, writes the summed durations in milliseconds
+ * of the norm pass, the finalize and the update to ms_sums[3] (host), the number of
+ * recorded steps to *steps, and stops recording.  Errors: NEOX_EINVAL, NEOX_ENOMEM,
+ * NEOX_EHIP. */
+int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps);
+int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);
+
+/* Text of the last error raised on the calling thread (never NULL). */
+const char* neox_zero1_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

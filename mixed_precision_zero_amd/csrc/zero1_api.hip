@@ -1,0 +1,452 @@
+// zero1_api.hip -- host side of the C ABI declared in include/neox_zero1.h:
+// argument validation, the ZeRO-1 shard partition, the chunk table, device scratch,
+// kernel launches and state readback.
+#include "neox_zero1.h"
+#include "zero1_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using namespace nz1;
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(NEOX_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr uint32_t kDefaultChunk = 8192;
+constexpr uint32_t kNormBlocksPerCU = 8;
+
+struct TimingSlot {
+    hipEvent_t ev[4];
+};
+
+}  // namespace
+
+struct neox_zero1 {
+    neox_zero1_config cfg;
+    int device = 0;
+    uint32_t nchunks = 0;
+    uint32_t norm_blocks = 0;
+    Chunk* d_chunks = nullptr;
+    double* d_partial = nullptr;
+    DevState* d_state = nullptr;
+    hipStream_t last_stream = nullptr;
+    FinalizeArgs fin{};
+    UpdateArgs upd_base{};
+    // profiling
+    std::vector<TimingSlot> timing;
+    int64_t timing_used = 0;
+};
+
+// ------------------------------------------------------------------------------------
+// configuration
+// ------------------------------------------------------------------------------------
+extern "C" int neox_zero1_default_config(neox_zero1_config* cfg) {
+    if (!cfg) return fail(NEOX_EINVAL, "cfg is NULL");
+    std::memset(cfg, 0, sizeof *cfg);
+    cfg->beta1 = 0.9;
+    cfg->beta2 = 0.95;
+    cfg->eps = 1e-8;
+    cfg->weight_decay = 0.01;
+    cfg->clip_norm = 1.0;
+    cfg->predivide_factor = 1.0;
+    cfg->dp_world_size = 1;
+    cfg->dtype = NEOX_F16;
+    cfg->scaler_mode = NEOX_SCALER_DYNAMIC;
+    cfg->growth_interval = 1000;
+    cfg->init_scale = 65536.0;
+    cfg->growth_factor = 2.0;
+    cfg->backoff_factor = 0.5;
+    cfg->min_scale = 1.0;
+    return NEOX_OK;
+}
+
+static bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
+
+static int validate_config(const neox_zero1_config* c) {
+    if (!(c->beta1 >= 0.0 && c->beta1 < 1.0)) return fail(NEOX_EINVAL, "beta1 %g not in [0,1)", c->beta1);
+    if (!(c->beta2 >= 0.0 && c->beta2 < 1.0)) return fail(NEOX_EINVAL, "beta2 %g not in [0,1)", c->beta2);
+    if (!(std::isfinite(c->eps) && c->eps >= 0.0)) return fail(NEOX_EINVAL, "eps %g", c->eps);
+    if (!(std::isfinite(c->weight_decay) && c->weight_decay >= 0.0))
+        return fail(NEOX_EINVAL, "weight_decay %g", c->weight_decay);
+    if (std::isnan(c->clip_norm) || std::isinf(c->clip_norm))
+        return fail(NEOX_EINVAL, "clip_norm %g", c->clip_norm);
+    if (!finite_pos(c->predivide_factor)) return fail(NEOX_EINVAL, "predivide_factor %g", c->predivide_factor);
+    if (c->dp_world_size < 1) return fail(NEOX_EINVAL, "dp_world_size %d", c->dp_world_size);
+    if (c->dtype != NEOX_F16 && c->dtype != NEOX_BF16) return fail(NEOX_EINVAL, "dtype %d", c->dtype);
+    if (c->scaler_mode != NEOX_SCALER_DYNAMIC && c->scaler_mode != NEOX_SCALER_STATIC)
+        return fail(NEOX_EINVAL, "scaler_mode %d", c->scaler_mode);
+    if (c->growth_interval < 1) return fail(NEOX_EINVAL, "growth_interval %d", c->growth_interval);
+    if (!finite_pos(c->init_scale) || !std::isfinite((float)c->init_scale) || (float)c->init_scale <= 0.0f)
+        return fail(NEOX_EINVAL, "init_scale %g", c->init_scale);
+    if (!(std::isfinite(c->growth_factor) && c->growth_factor >= 1.0))
+        return fail(NEOX_EINVAL, "growth_factor %g", c->growth_factor);
+    if (!(c->backoff_factor > 0.0 && c->backoff_factor <= 1.0))
+        return fail(NEOX_EINVAL, "backoff_factor %g", c->backoff_factor);
+    if (!finite_pos(c->min_scale) || (float)c->min_scale <= 0.0f || !std::isfinite((float)c->min_scale))
+        return fail(NEOX_EINVAL, "min_scale %g", c->min_scale);
+    if (c->init_step < 0 || c->init_skipped < 0 || c->init_good_steps < 0 ||
+        c->init_consecutive_overflows < 0)
+        return fail(NEOX_EINVAL, "negative resume counter");
+    if (c->chunk_elems != 0 &&
+        (c->chunk_elems % kVec != 0 || c->chunk_elems < 256 || c->chunk_elems > (1u << 24)))
+        return fail(NEOX_EINVAL, "chunk_elems %u: multiple of 8 in [256, 2^24]", c->chunk_elems);
+    if (c->norm_blocks > (1u << 20)) return fail(NEOX_EINVAL, "norm_blocks %u too large", c->norm_blocks);
+    return NEOX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// shard partition: interval intersection of each tensor with the rank's range
+// ------------------------------------------------------------------------------------
+extern "C" int neox_zero1_partition(const uint64_t* tensor_numel, const uint8_t* tensor_decay,
+                                    uint64_t ntensors, uint32_t dp_world_size, uint32_t rank,
+                                    uint32_t align, neox_shard_segment* out, uint64_t cap,
+                                    uint64_t* nseg_out, uint64_t* shard_numel_out) {
+    if (!nseg_out || !shard_numel_out) return fail(NEOX_EINVAL, "null output pointer");
+    if (ntensors && (!tensor_numel || !tensor_decay)) return fail(NEOX_EINVAL, "null tensor list");
+    if (cap && !out) return fail(NEOX_EINVAL, "out is NULL with cap > 0");
+    if (dp_world_size == 0 || align == 0) return fail(NEOX_EINVAL, "dp_world_size and align must be >= 1");
+    if (rank >= dp_world_size) return fail(NEOX_EINVAL, "rank %u >= dp_world_size %u", rank, dp_world_size);
+    uint64_t total = 0;
+    for (uint64_t i = 0; i < ntensors; ++i) {
+        if (tensor_numel[i] > UINT64_MAX - total) return fail(NEOX_EINVAL, "total numel overflows");
+        total += tensor_numel[i];
+    }
+    const unsigned __int128 unit = (unsigned __int128)dp_world_size * align;
+    const unsigned __int128 padded128 = ((unsigned __int128)total + unit - 1) / unit * unit;
+    if (padded128 > UINT64_MAX) return fail(NEOX_EINVAL, "padded numel overflows");
+    const uint64_t padded = (uint64_t)padded128;
+    const uint64_t P = padded / dp_world_size;
+    const uint64_t lo = (uint64_t)rank * P, hi = lo + P;
+
+    uint64_t n = 0;
+    auto emit = [&](uint64_t a, uint64_t b, uint64_t tensor_start, uint32_t tid, uint32_t flags) {
+        if (n < cap) {
+            out[n].shard_offset = a - lo;
+            out[n].numel = b - a;
+            out[n].tensor_offset = a - tensor_start;
+            out[n].tensor_id = tid;
+            out[n].flags = flags;
+        }
+        ++n;
+    };
+    uint64_t off = 0;
+    for (uint64_t i = 0; i < ntensors && off < hi; ++i) {
+        const uint64_t a = off > lo ? off : lo;
+        const uint64_t end = off + tensor_numel[i];
+        const uint64_t b = end < hi ? end : hi;
+        if (a < b) emit(a, b, off, (uint32_t)i, tensor_decay[i] ? NEOX_SEG_DECAY : 0u);
+        off = end;
+    }
+    {
+        const uint64_t a = total > lo ? total : lo;
+        const uint64_t b = padded < hi ? padded : hi;
+        if (a < b) emit(a, b, total, NEOX_PAD_TENSOR, 0u);
+    }
+    *nseg_out = n;
+    *shard_numel_out = P;
+    return NEOX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// chunk table
+// ------------------------------------------------------------------------------------
+static bool aligned16(uintptr_t p) { return (p & 15u) == 0; }
+
+// Smallest head h in [0, 8) after which all five arrays are 16-byte aligned, or -1.
+static int vector_head(const neox_segment& s) {
+    for (int h = 0; h < kVec; ++h) {
+        if (aligned16((uintptr_t)s.grad + 2u * h) && aligned16((uintptr_t)s.half + 2u * h) &&
+            aligned16((uintptr_t)s.master + 4u * h) && aligned16((uintptr_t)s.exp_avg + 4u * h) &&
+            aligned16((uintptr_t)s.exp_avg_sq + 4u * h))
+            return h;
+    }
+    return -1;
+}
+
+static void push_chunk(std::vector<Chunk>& t, const neox_segment& s, uint32_t seg, uint64_t start,
+                       uint32_t len, bool vec) {
+    Chunk c{};
+    c.grad = static_cast<const uint16_t*>(s.grad) + start;
+    c.half = static_cast<uint16_t*>(s.half) + start;
+    c.master = s.master + start;
+    c.m = s.exp_avg + start;
+    c.v = s.exp_avg_sq + start;
+    c.len = len;
+    c.flags = ((s.flags & NEOX_SEG_DECAY) ? CH_DECAY : 0u) | (vec ? CH_VEC : 0u);
+    c.seg = seg;
+    t.push_back(c);
+}
+
+static void build_chunks(const neox_segment* segs, uint64_t nseg, uint32_t C, std::vector<Chunk>& t) {
+    for (uint64_t s = 0; s < nseg; ++s) {
+        const neox_segment& sg = segs[s];
+        const int head = vector_head(sg);
+        uint64_t off = 0;
+        if (head > 0) {
+            const uint64_t h = (uint64_t)head < sg.numel ? (uint64_t)head : sg.numel;
+            push_chunk(t, sg, (uint32_t)s, 0, (uint32_t)h, false);
+            off = h;
+        }
+        while (off < sg.numel) {
+            const uint64_t len = sg.numel - off < C ? sg.numel - off : C;
+            push_chunk(t, sg, (uint32_t)s, off, (uint32_t)len, head >= 0);
+            off += len;
+        }
+    }
+}
+
+static bool overlaps(uintptr_t a, uint64_t abytes, uintptr_t b, uint64_t bbytes) {
+    return a < b + bbytes && b < a + abytes;
+}
+
+static int validate_segments(const neox_segment* segs, uint64_t nseg) {
+    if (!segs) return fail(NEOX_EINVAL, "segs is NULL");
+    if (nseg == 0) return fail(NEOX_EINVAL, "nseg is 0");
+    if (nseg > (1u << 31)) return fail(NEOX_EINVAL, "too many segments");
+    struct Range { uintptr_t p; uint64_t bytes; uint64_t seg; };
+    std::vector<Range> ranges;
+    ranges.reserve(nseg * 5);
+    for (uint64_t i = 0; i < nseg; ++i) {
+        const neox_segment& s = segs[i];
+        if (!s.grad || !s.half || !s.master || !s.exp_avg || !s.exp_avg_sq)
+            return fail(NEOX_EINVAL, "segment %llu: null array", (unsigned long long)i);
+        if (s.numel == 0) return fail(NEOX_EINVAL, "segment %llu: numel is 0", (unsigned long long)i);
+        if (s.numel > (UINT64_MAX >> 3)) return fail(NEOX_EINVAL, "segment %llu: numel too large", (unsigned long long)i);
+        if (((uintptr_t)s.grad & 1u) || ((uintptr_t)s.half & 1u))
+            return fail(NEOX_EINVAL, "segment %llu: grad/half not 2-byte aligned", (unsigned long long)i);
+        if (((uintptr_t)s.master & 3u) || ((uintptr_t)s.exp_avg & 3u) || ((uintptr_t)s.exp_avg_sq & 3u))
+            return fail(NEOX_EINVAL, "segment %llu: FP32 array not 4-byte aligned", (unsigned long long)i);
+        if (s.flags & ~NEOX_SEG_DECAY) return fail(NEOX_EINVAL, "segment %llu: unknown flags", (unsigned long long)i);
+        ranges.push_back({(uintptr_t)s.half, 2 * s.numel, i});
+        ranges.push_back({(uintptr_t)s.master, 4 * s.numel, i});
+        ranges.push_back({(uintptr_t)s.exp_avg, 4 * s.numel, i});
+        ranges.push_back({(uintptr_t)s.exp_avg_sq, 4 * s.numel, i});
+    }
+    // written arrays must not overlap each other (sorted sweep)
+    std::sort(ranges.begin(), ranges.end(), [](const Range& a, const Range& b) { return a.p < b.p; });
+    for (size_t k = 1; k < ranges.size(); ++k)
+        if (overlaps(ranges[k - 1].p, ranges[k - 1].bytes, ranges[k].p, ranges[k].bytes))
+            return fail(NEOX_EINVAL, "segments %llu and %llu: written arrays overlap",
+                        (unsigned long long)ranges[k - 1].seg, (unsigned long long)ranges[k].seg);
+    return NEOX_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// create / step / state / destroy
+// ------------------------------------------------------------------------------------
+static void free_handle(neox_zero1* h) {
+    if (!h) return;
+    for (auto& s : h->timing)
+        for (auto& e : s.ev)
+            if (e) (void)hipEventDestroy(e);
+    if (h->d_chunks) (void)hipFree(h->d_chunks);
+    if (h->d_partial) (void)hipFree(h->d_partial);
+    if (h->d_state) (void)hipFree(h->d_state);
+    delete h;
+}
+
+extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs,
+                                 uint64_t nseg, void* hip_stream, neox_zero1** out) {
+    if (!out) return fail(NEOX_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!cfg) return fail(NEOX_EINVAL, "cfg is NULL");
+    int rc = validate_config(cfg);
+    if (rc) return rc;
+    rc = validate_segments(segs, nseg);
+    if (rc) return rc;
+
+    const uint32_t C = cfg->chunk_elems ? cfg->chunk_elems : kDefaultChunk;
+    std::vector<Chunk> table;
+    try {
+        build_chunks(segs, nseg, C, table);
+    } catch (const std::bad_alloc&) {
+        return fail(NEOX_ENOMEM, "host allocation of the chunk table");
+    }
+    if (table.size() >= (1ull << 24)) return fail(NEOX_EINVAL, "%zu chunks: raise chunk_elems", table.size());
+
+    neox_zero1* h = new (std::nothrow) neox_zero1();
+    if (!h) return fail(NEOX_ENOMEM, "host allocation of the handle");
+    h->cfg = *cfg;
+    h->nchunks = (uint32_t)table.size();
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) { free_handle(h); return hip_fail(e, "hipGetDevice"); }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess) { free_handle(h); return hip_fail(e, "hipDeviceGetAttribute"); }
+    uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : (uint32_t)cus * kNormBlocksPerCU;
+    if (nb > h->nchunks) nb = h->nchunks;
+    if (nb == 0) nb = 1;
+    h->norm_blocks = nb;
+
+    e = hipMalloc(&h->d_chunks, table.size() * sizeof(Chunk));
+    if (e == hipSuccess) e = hipMalloc(&h->d_partial, nb * sizeof(double));
+    if (e == hipSuccess) e = hipMalloc(&h->d_state, sizeof(DevState));
+    if (e != hipSuccess) {
+        free_handle(h);
+        return e == hipErrorOutOfMemory ? fail(NEOX_ENOMEM, "hipMalloc of library scratch")
+                                        : hip_fail(e, "hipMalloc");
+    }
+
+    DevState st{};
+    st.loss_scale = (float)cfg->init_scale;
+    st.good_steps = cfg->init_good_steps;
+    st.step = cfg->init_step;
+    st.skipped_total = cfg->init_skipped;
+    st.consecutive_overflows = cfg->init_consecutive_overflows;
+    st.last_skipped = 0;
+    st.last_sumsq = 0.0;
+    st.last_grad_norm = 0.0f;
+    st.last_clip_coef = 1.0f;
+    st.inv = unscale_factor(cfg->predivide_factor, (double)cfg->dp_world_size, st.loss_scale);
+    st.skip = 1;
+
+    e = hipMemcpyAsync(h->d_chunks, table.data(), table.size() * sizeof(Chunk), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->d_state, &st, sizeof st, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) { free_handle(h); return hip_fail(e, "upload of the chunk table"); }
+
+    FinalizeArgs& f = h->fin;
+    f.clip_norm = cfg->clip_norm;
+    f.beta1 = cfg->beta1;
+    f.beta2 = cfg->beta2;
+    f.growth_factor = cfg->growth_factor;
+    f.backoff_factor = cfg->backoff_factor;
+    f.predivide_factor = cfg->predivide_factor;
+    f.dp_world_size = (double)cfg->dp_world_size;
+    f.min_scale = (float)cfg->min_scale;
+    f.dynamic = cfg->scaler_mode == NEOX_SCALER_DYNAMIC;
+    f.growth_interval = cfg->growth_interval;
+
+    UpdateArgs& u = h->upd_base;
+    u.b1 = (float)cfg->beta1;
+    u.omb1 = (float)(1.0 - cfg->beta1);
+    u.b2 = (float)cfg->beta2;
+    u.omb2 = (float)(1.0 - cfg->beta2);
+    u.eps = (float)cfg->eps;
+    u.wd = (float)cfg->weight_decay;
+    u.lr = 0.0f;
+
+    h->last_stream = stream;
+    *out = h;
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
+    if (!h) return fail(NEOX_EINVAL, "handle is NULL");
+    if (!std::isfinite(lr)) return fail(NEOX_EINVAL, "lr %g is not finite", (double)lr);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    UpdateArgs u = h->upd_base;
+    u.lr = lr;
+    TimingSlot* ts = nullptr;
+    if (h->timing_used < (int64_t)h->timing.size()) ts = &h->timing[h->timing_used++];
+
+    hipError_t e = hipSuccess;
+    if (ts) e = hipEventRecord(ts->ev[0], stream);
+    if (e == hipSuccess)
+        e = launch_norm(h->cfg.dtype, h->d_chunks, h->nchunks, h->norm_blocks, h->d_state,
+                        h->d_partial, stream);
+    if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[1], stream);
+    if (e == hipSuccess) e = launch_finalize(h->d_partial, h->norm_blocks, h->d_state, h->fin, stream);
+    if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[2], stream);
+    if (e == hipSuccess) e = launch_update(h->cfg.dtype, h->d_chunks, h->nchunks, h->d_state, u, stream);
+    if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[3], stream);
+    h->last_stream = stream;
+    if (e != hipSuccess) return hip_fail(e, "step launch");
+    return NEOX_OK;
+}
+
+extern "C" int neox_scaler_state(neox_zero1* h, neox_scaler_state_t* out) {
+    if (!h || !out) return fail(NEOX_EINVAL, "null argument");
+    hipError_t e = hipStreamSynchronize(h->last_stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    DevState st;
+    e = hipMemcpy(&st, h->d_state, sizeof st, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "state readback");
+    out->loss_scale = st.loss_scale;
+    out->good_steps = st.good_steps;
+    out->step = st.step;
+    out->skipped_total = st.skipped_total;
+    out->consecutive_overflows = st.consecutive_overflows;
+    out->last_skipped = st.last_skipped;
+    out->last_grad_norm = st.last_grad_norm;
+    out->last_clip_coef = st.last_clip_coef;
+    out->last_sumsq = st.last_sumsq;
+    out->device_loss_scale = &h->d_state->loss_scale;
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_destroy(neox_zero1* h) {
+    if (!h) return NEOX_OK;
+    hipError_t e = hipStreamSynchronize(h->last_stream);
+    free_handle(h);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps) {
+    if (!h || max_steps < 1 || max_steps > 1000000) return fail(NEOX_EINVAL, "bad timing request");
+    for (auto& s : h->timing)
+        for (auto& e : s.ev) (void)hipEventDestroy(e);
+    h->timing.clear();
+    h->timing_used = 0;
+    try {
+        h->timing.resize(max_steps);
+    } catch (const std::bad_alloc&) {
+        return fail(NEOX_ENOMEM, "timing slots");
+    }
+    for (auto& s : h->timing)
+        for (auto& e : s.ev) e = nullptr;
+    for (auto& s : h->timing)
+        for (auto& e : s.ev) {
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return hip_fail(r, "hipEventCreate");
+        }
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps) {
+    if (!h || !ms_sums || !steps) return fail(NEOX_EINVAL, "null argument");
+    ms_sums[0] = ms_sums[1] = ms_sums[2] = 0.0;
+    for (int64_t i = 0; i < h->timing_used; ++i) {
+        auto& s = h->timing[i];
+        hipError_t r = hipEventSynchronize(s.ev[3]);
+        if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+        for (int k = 0; k < 3; ++k) {
+            float ms = 0.0f;
+            r = hipEventElapsedTime(&ms, s.ev[k], s.ev[k + 1]);
+            if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+            ms_sums[k] += ms;
+        }
+    }
+    *steps = h->timing_used;
+    for (auto& s : h->timing)
+        for (auto& e : s.ev) (void)hipEventDestroy(e);
+    h->timing.clear();
+    h->timing_used = 0;
+    return NEOX_OK;
+}
+
+extern "C" const char* neox_zero1_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,85 @@
+// zero1_internal.h -- types shared by the host side and the gfx950 kernels of the
+// ZeRO-1 mixed-precision Adam step.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nz1 {
+
+constexpr int kBlock = 256;   // threads per block: 4 wave64s
+constexpr int kVec = 8;       // elements per thread-vector: one 16-byte load of halves
+
+enum : uint32_t {
+    CH_DECAY = 1u,   // elements of this chunk receive decoupled weight decay
+    CH_VEC = 2u,     // all five arrays are 16-byte aligned at the chunk start
+};
+
+// One unit of work: up to chunk_elems consecutive elements of one segment.  The five
+// pointers already point at the chunk's first element, so a block needs a single
+// 64-byte scalar load to find its work.
+struct alignas(64) Chunk {
+    const uint16_t* grad;
+    uint16_t* half;
+    float* master;
+    float* m;
+    float* v;
+    uint32_t len;
+    uint32_t flags;
+    uint32_t seg;
+    uint32_t pad_;
+};
+static_assert(sizeof(Chunk) == 64, "Chunk is one 64-byte scalar load");
+
+// Device-resident step state.  The host never needs to know whether a step was
+// skipped: the finalize kernel writes the decision here and the update kernel reads it.
+struct alignas(64) DevState {
+    // persistent scaler / optimizer counters
+    float loss_scale;            // scale the next gradient carries
+    int32_t good_steps;
+    int64_t step;                // applied steps t
+    int64_t skipped_total;
+    int32_t consecutive_overflows;
+    int32_t last_skipped;
+    double last_sumsq;
+    float last_grad_norm;
+    float last_clip_coef;
+    // handed from the finalize to the passes
+    float inv;                   // fp32(f / (D * S)) for the next norm pass
+    float gscale;                // this step's unscale factor times clip coefficient
+    float rbc1;                  // 1 / (1 - beta1^t)
+    float rsbc2;                 // 1 / sqrt(1 - beta2^t)
+    int32_t skip;                // this step's decision
+    int32_t pad_;
+};
+
+struct FinalizeArgs {
+    double clip_norm;
+    double beta1, beta2;
+    double growth_factor, backoff_factor;
+    double predivide_factor;
+    double dp_world_size;
+    float min_scale;
+    int32_t dynamic;
+    int32_t growth_interval;
+};
+
+struct UpdateArgs {
+    float b1, omb1, b2, omb2, eps, wd, lr;
+};
+
+// Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
+hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
+                       const DevState* st, double* partial, hipStream_t stream);
+hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
+                           const FinalizeArgs& a, hipStream_t stream);
+hipError_t launch_update(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
+                         const UpdateArgs& a, hipStream_t stream);
+
+// The unscale factor for scale s, computed in double and rounded once to FP32; the
+// host (initial state) and the finalize kernel evaluate the same expression.
+__host__ __device__ inline float unscale_factor(double predivide, double dp, float s) {
+    return (float)(predivide / (dp * (double)s));
+}
+
+}  // namespace nz1

@@ -1,0 +1,329 @@
+// zero1_kernels.hip -- gfx950 kernels of the ZeRO-1 mixed-precision Adam step.
+//
+// Three launches per step, all on the caller's stream:
+//   norm      persistent grid; every block walks a fixed, strided set of chunks and
+//             accumulates the squares of the unscaled FP32 gradient in double.  A
+//             non-finite unscaled value makes its square, and so the block's sum,
+//             non-finite; finite values cannot overflow a double sum (|g| < 2^128 so
+//             g^2 < 2^256), so "sum not finite" is exactly "some gradient overflowed".
+//   finalize  one block; fixed-order sum of the per-block partials, then the skip
+//             decision, clip coefficient, step count, bias corrections and the loss
+//             scale update, written to the device state block.
+//   update    one block per chunk; returns at once on a skipped step, otherwise
+//             unscale + clip + AdamW + cast with 16-byte loads and stores.
+// Sources: FP32 Adam state with FP16 weights and dynamic loss scaling [OPT: Open
+// Pre-trained Transformer Language Models, paper card, 计算设置]; pre-divide factor
+// and clipping at 1.0 / 0.3 [same card, 方法适配]; each rank updates only its shard
+// [GPT-NeoX democratisation article, 技术深度解析].  Formulas: Adam with bias
+// correction (Kingma & Ba), decoupled decay (Loshchilov & Hutter), loss scaling
+// (Micikevicius et al. 2018).
+#include "zero1_internal.h"
+
+namespace nz1 {
+
+// ------------------------------------------------------------------------------------
+// Half formats.  Decoding is exact; encoding rounds to nearest even in hardware
+// (v_cvt_f16_f32 under the default rounding mode, v_cvt_pk_bf16_f32 on gfx950).
+// ------------------------------------------------------------------------------------
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Fmt;
+
+template <>
+struct Fmt<1> {
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+    static __device__ __forceinline__ float one(uint16_t b) {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        f16x2 p = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, p);
+    }
+    static __device__ __forceinline__ uint16_t enc(float a) {
+        return __builtin_bit_cast(uint16_t, (_Float16)a);
+    }
+};
+
+template <>
+struct Fmt<2> {
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    static __device__ __forceinline__ float one(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        bf16x2 p = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, p);
+    }
+    static __device__ __forceinline__ uint16_t enc(float a) {
+        return __builtin_bit_cast(uint16_t, (__bf16)a);
+    }
+};
+
+// ------------------------------------------------------------------------------------
+// Deterministic block reduction of a double: xor-butterfly inside each wave64 (every
+// lane ends with the same, order-fixed value), then wave 0..3 partials in index order.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ double block_sum(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    __shared__ double ws[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = ws[0];
+#pragma unroll
+    for (int k = 1; k < kBlock / 64; ++k) r += ws[k];
+    return r;
+}
+
+// ------------------------------------------------------------------------------------
+// norm: sum over the shard of fp64(fp32(x * inv))^2
+// ------------------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void sq8(const uint4 q, float inv, double& a0, double& a1) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const double x = (double)(Fmt<DT>::lo(w[k]) * inv);
+        const double y = (double)(Fmt<DT>::hi(w[k]) * inv);
+        a0 = __builtin_fma(x, x, a0);
+        a1 = __builtin_fma(y, y, a1);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ chunks,
+                                                      uint32_t nchunks,
+                                                      const DevState* __restrict__ st,
+                                                      double* __restrict__ partial) {
+    const float inv = st->inv;
+    double a0 = 0.0, a1 = 0.0;
+    for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const Chunk* ch = chunks + c;
+        const uint16_t* __restrict__ g = ch->grad;
+        const uint32_t len = ch->len;
+        uint32_t done = 0;
+        if (ch->flags & CH_VEC) {
+            const uint4* __restrict__ g4 = reinterpret_cast<const uint4*>(g);
+            const uint32_t nvec = len / kVec;
+            uint32_t i = threadIdx.x;
+            for (; i + 3 * kBlock < nvec; i += 4 * kBlock) {
+                const uint4 q0 = g4[i];
+                const uint4 q1 = g4[i + kBlock];
+                const uint4 q2 = g4[i + 2 * kBlock];
+                const uint4 q3 = g4[i + 3 * kBlock];
+                sq8<DT>(q0, inv, a0, a1);
+                sq8<DT>(q1, inv, a0, a1);
+                sq8<DT>(q2, inv, a0, a1);
+                sq8<DT>(q3, inv, a0, a1);
+            }
+            for (; i < nvec; i += kBlock) sq8<DT>(g4[i], inv, a0, a1);
+            done = nvec * kVec;
+        }
+        for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
+            const double x = (double)(Fmt<DT>::one(g[i]) * inv);
+            a0 = __builtin_fma(x, x, a0);
+        }
+    }
+    const double s = block_sum(a0 + a1);
+    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+// ------------------------------------------------------------------------------------
+// finalize: one block
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ bool f64_finite(double x) {
+    return (__double_as_longlong(x) & 0x7FF0000000000000ll) != 0x7FF0000000000000ll;
+}
+__device__ __forceinline__ bool f32_finite(float x) {
+    return (__float_as_uint(x) & 0x7F800000u) != 0x7F800000u;
+}
+
+__global__ __launch_bounds__(kBlock) void finalize_kernel(const double* __restrict__ partial,
+                                                          uint32_t nparts,
+                                                          DevState* __restrict__ st,
+                                                          FinalizeArgs a) {
+    double acc = 0.0;
+    for (uint32_t i = threadIdx.x; i < nparts; i += kBlock) acc += partial[i];
+    const double sumsq = block_sum(acc);
+    if (threadIdx.x != 0) return;
+
+    float scale = st->loss_scale;
+    const float inv_used = st->inv;
+    if (!f64_finite(sumsq)) {
+        // overflow: skip, back off (not below the floor), restart the clean count
+        st->skip = 1;
+        if (a.dynamic) {
+            float s = (float)((double)scale * a.backoff_factor);
+            scale = s < a.min_scale ? a.min_scale : s;
+        }
+        st->good_steps = 0;
+        st->consecutive_overflows += 1;
+        st->skipped_total += 1;
+        st->last_skipped = 1;
+        st->last_sumsq = 0.0;
+        st->last_grad_norm = __builtin_inff();
+        st->last_clip_coef = 1.0f;
+    } else {
+        const double norm = __builtin_sqrt(sumsq);
+        double coef = 1.0;
+        if (a.clip_norm > 0.0 && norm > a.clip_norm) coef = a.clip_norm / norm;
+        const int64_t t = st->step + 1;
+        const double bc1 = 1.0 - pow(a.beta1, (double)t);
+        const double bc2 = 1.0 - pow(a.beta2, (double)t);
+        st->skip = 0;
+        st->gscale = (float)((double)inv_used * coef);
+        st->rbc1 = (float)(1.0 / bc1);
+        st->rsbc2 = (float)(1.0 / __builtin_sqrt(bc2));
+        st->step = t;
+        int32_t good = st->good_steps + 1;
+        if (a.dynamic && good >= a.growth_interval) {
+            const float s = (float)((double)scale * a.growth_factor);
+            if (f32_finite(s)) scale = s;
+            good = 0;
+        }
+        st->good_steps = good;
+        st->consecutive_overflows = 0;
+        st->last_skipped = 0;
+        st->last_sumsq = sumsq;
+        st->last_grad_norm = (float)norm;
+        st->last_clip_coef = (float)coef;
+    }
+    st->loss_scale = scale;
+    st->inv = unscale_factor(a.predivide_factor, a.dp_world_size, scale);
+}
+
+// ------------------------------------------------------------------------------------
+// update: fused unscale + clip + AdamW + cast, one block per chunk
+// ------------------------------------------------------------------------------------
+struct Coefs {
+    float gs, rbc1, rsbc2;
+};
+
+__device__ __forceinline__ void adam(float h, float& w, float& m, float& v, const Coefs& c,
+                                     const UpdateArgs& a, bool decay) {
+    const float g = h * c.gs;
+    m = __builtin_fmaf(a.b1, m, a.omb1 * g);
+    v = __builtin_fmaf(a.b2, v, a.omb2 * (g * g));
+    const float den = __builtin_fmaf(__builtin_sqrtf(v), c.rsbc2, a.eps);
+    float u = (m * c.rbc1) / den;
+    if (decay) u = __builtin_fmaf(a.wd, w, u);
+    w = __builtin_fmaf(-a.lr, u, w);
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict__ chunks,
+                                                        const DevState* __restrict__ st,
+                                                        UpdateArgs a) {
+    if (st->skip) return;
+    const Chunk* ch = chunks + blockIdx.x;
+    const uint32_t len = ch->len;
+    const uint32_t flags = ch->flags;
+    const bool decay = (flags & CH_DECAY) != 0;
+    const uint16_t* __restrict__ gp = ch->grad;
+    uint16_t* __restrict__ hp = ch->half;
+    float* __restrict__ wp = ch->master;
+    float* __restrict__ mp = ch->m;
+    float* __restrict__ vp = ch->v;
+    const Coefs c{st->gscale, st->rbc1, st->rsbc2};
+
+    uint32_t done = 0;
+    if (flags & CH_VEC) {
+        const uint4* __restrict__ g4 = reinterpret_cast<const uint4*>(gp);
+        uint4* __restrict__ h4 = reinterpret_cast<uint4*>(hp);
+        float4* __restrict__ w4 = reinterpret_cast<float4*>(wp);
+        float4* __restrict__ m4 = reinterpret_cast<float4*>(mp);
+        float4* __restrict__ v4 = reinterpret_cast<float4*>(vp);
+        const uint32_t nvec = len / kVec;
+        for (uint32_t base = 0; base < nvec; base += U * kBlock) {
+            uint4 G[U];
+            float4 W[U][2], M[U][2], V[U][2];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = base + u * kBlock + threadIdx.x;
+                if (i < nvec) {
+                    G[u] = g4[i];
+                    W[u][0] = w4[2 * i];
+                    W[u][1] = w4[2 * i + 1];
+                    M[u][0] = m4[2 * i];
+                    M[u][1] = m4[2 * i + 1];
+                    V[u][0] = v4[2 * i];
+                    V[u][1] = v4[2 * i + 1];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = base + u * kBlock + threadIdx.x;
+                if (i < nvec) {
+                    const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
+                    float w[8] = {W[u][0].x, W[u][0].y, W[u][0].z, W[u][0].w,
+                                  W[u][1].x, W[u][1].y, W[u][1].z, W[u][1].w};
+                    float m[8] = {M[u][0].x, M[u][0].y, M[u][0].z, M[u][0].w,
+                                  M[u][1].x, M[u][1].y, M[u][1].z, M[u][1].w};
+                    float v[8] = {V[u][0].x, V[u][0].y, V[u][0].z, V[u][0].w,
+                                  V[u][1].x, V[u][1].y, V[u][1].z, V[u][1].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        adam(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], v[2 * k], c, a, decay);
+                        adam(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], v[2 * k + 1], c, a,
+                             decay);
+                    }
+                    w4[2 * i] = make_float4(w[0], w[1], w[2], w[3]);
+                    w4[2 * i + 1] = make_float4(w[4], w[5], w[6], w[7]);
+                    m4[2 * i] = make_float4(m[0], m[1], m[2], m[3]);
+                    m4[2 * i + 1] = make_float4(m[4], m[5], m[6], m[7]);
+                    v4[2 * i] = make_float4(v[0], v[1], v[2], v[3]);
+                    v4[2 * i + 1] = make_float4(v[4], v[5], v[6], v[7]);
+                    h4[i] = make_uint4(Fmt<DT>::pack(w[0], w[1]), Fmt<DT>::pack(w[2], w[3]),
+                                       Fmt<DT>::pack(w[4], w[5]), Fmt<DT>::pack(w[6], w[7]));
+                }
+            }
+        }
+        done = nvec * kVec;
+    }
+    // scalar path: chunks that are not 16-byte aligned, and the last < 8 elements
+    for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
+        float w = wp[i], m = mp[i], v = vp[i];
+        adam(Fmt<DT>::one(gp[i]), w, m, v, c, a, decay);
+        wp[i] = w;
+        mp[i] = m;
+        vp[i] = v;
+        hp[i] = Fmt<DT>::enc(w);
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------
+constexpr int kUpdateUnroll = 2;
+
+hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
+                       const DevState* st, double* partial, hipStream_t stream) {
+    if (dtype == 1)
+        norm_kernel<1><<<blocks, kBlock, 0, stream>>>(chunks, nchunks, st, partial);
+    else
+        norm_kernel<2><<<blocks, kBlock, 0, stream>>>(chunks, nchunks, st, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
+                           const FinalizeArgs& a, hipStream_t stream) {
+    finalize_kernel<<<1, kBlock, 0, stream>>>(partial, nparts, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_update(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
+                         const UpdateArgs& a, hipStream_t stream) {
+    if (dtype == 1)
+        update_kernel<1, kUpdateUnroll><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+    else
+        update_kernel<2, kUpdateUnroll><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace nz1

@@ -1,0 +1,189 @@
+"""GPU parity of the step against the oracle on small and mid-size shards.
+
+Every case runs the library through its C ABI on the same bytes the oracle reads and
+compares every element (see gpu_harness for the tolerances)."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_zero_amd as Z
+import workloads as W
+from gpu_harness import Checker, DeviceShard, lib_config, log
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sequence(w, steps, lr=None, shard=None, where="", **cfg_over):
+    shard = shard or DeviceShard(w)
+    shard.init_()
+    chk = Checker(shard, **cfg_over)
+    lr = w.hyper.lr if lr is None else lr
+    try:
+        for k in range(steps):
+            shard.grads_(k, chk.scale())
+            chk.step(lr, where=f"{where} step {k}")
+    finally:
+        chk.close()
+    return chk
+
+
+def test_tiny_1m_sequence():
+    """1,048,576 params, 10 steps, +inf at element 777,777 on step 5: the skip leaves
+    every array untouched and halves the scale; all other steps match elementwise."""
+    w = W.tiny()
+    log("case tiny_1m")
+    chk = run_sequence(w, w.steps, where="tiny_1m")
+    assert chk.ost.skipped_total == 1 and chk.ost.step == 9
+    assert chk.ost.loss_scale == 32768.0
+
+
+def _custom(name, sizes, decays, dtype=W.F16, **hy):
+    hyper = W.Hyper(dtype=dtype, **hy)
+    if dtype == W.BF16:
+        hyper.scaler_mode = hy.get("scaler_mode", W.STATIC)
+        hyper.init_scale = hy.get("init_scale", 1.0)
+    return W.Workload(name, 900, list(zip(sizes, decays)), hyper, steps=4)
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("misalign", [(0, 0, 0, 0, 0), (3, 3, 3, 3, 3), (1, 2, 0, 3, 1)],
+                         ids=["aligned", "same_offset", "mixed_offsets"])
+def test_tiny_shards_bruteforce(dtype, misalign):
+    """Random segment splits of 1..64 elements, random decay flags, both half formats,
+    aligned / consistently offset / inconsistently offset arrays, and an inf or NaN
+    injected at a random element on one step."""
+    rng = np.random.default_rng(100 + dtype * 10 + sum(misalign))
+    for case in range(12):
+        n = int(rng.integers(1, 65))
+        cuts = sorted(set(int(c) for c in rng.integers(1, n, size=int(rng.integers(0, 4))))) if n > 1 else []
+        sizes = np.diff([0] + cuts + [n]).tolist()
+        decays = [bool(x) for x in rng.integers(0, 2, len(sizes))]
+        w = _custom(f"tiny{case}", sizes, decays, dtype, clip_norm=float(rng.choice([0.0, 1e-3, 1.0])))
+        w.grad_sigma = float(rng.choice([1e-4, 1e-2]))
+        kind = ["+inf", "-inf", "nan"][case % 3]
+        w.injections = {2: [(int(rng.integers(0, n)), kind)]}
+        log(f"case tiny dtype={dtype} misalign={misalign} n={n} sizes={sizes}")
+        chk = run_sequence(w, 4, shard=DeviceShard(w, flat=True, misalign=misalign),
+                           where=f" n={n}")
+        assert chk.ost.skipped_total == 1
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+def test_ragged_many_chunks(dtype):
+    """~70k elements in segments of awkward lengths, 256-element chunks (hundreds of
+    blocks, ragged tails) and a 3-block norm pass looping over them."""
+    sizes = [1, 7, 8, 9, 255, 256, 257, 4095, 4097, 12_345, 33_333, 8, 1000, 15_000]
+    decays = [i % 3 != 0 for i in range(len(sizes))]
+    w = _custom("ragged", sizes, decays, dtype)
+    log(f"case ragged dtype={dtype}")
+    run_sequence(w, 3, chunk_elems=256, norm_blocks=3, where=" ragged")
+    run_sequence(w, 2, shard=DeviceShard(w, flat=False, misalign=(1, 1, 1, 1, 1)),
+                 chunk_elems=512, where=" ragged separate")
+
+
+def _outputs(shard):
+    torch.cuda.synchronize()
+    return {k: torch.cat([s[k].reshape(-1) for s in shard.segs]).clone()
+            for k in ("half", "master", "m", "v")}
+
+
+def test_chunking_and_grid_independence_and_determinism():
+    """Elementwise outputs are bitwise independent of the chunk size and of the norm
+    pass's grid; the same configuration run twice is bitwise identical, norm included."""
+    sizes = [100_000, 3, 77_777, 8192, 1]
+    w = _custom("chunking", sizes, [True, False, True, False, True], clip_norm=0.01)
+    results = []
+    for chunk, blocks in ((0, 0), (0, 0), (256, 1), (1024, 7), (65536, 2)):
+        log(f"case chunking chunk={chunk} blocks={blocks}")
+        shard = DeviceShard(w)
+        shard.init_()
+        h = Z.neox_zero1_create(lib_config(w, chunk_elems=chunk, norm_blocks=blocks),
+                                shard.neox_segments(), torch.cuda.current_stream().cuda_stream)
+        norms = []
+        for k in range(3):
+            shard.grads_(k, Z.neox_scaler_state(h).loss_scale)
+            Z.neox_zero1_step(h, 1e-3, torch.cuda.current_stream().cuda_stream)
+            st = Z.neox_scaler_state(h)
+            norms.append((st.last_grad_norm, st.last_sumsq))
+        Z.neox_zero1_destroy(h)
+        results.append((_outputs(shard), norms))
+    base, base_norms = results[0]
+    again, again_norms = results[1]
+    for k in base:
+        assert torch.equal(base[k], again[k]), k
+    assert base_norms == again_norms
+    for out, norms in results[2:]:
+        for k in base:
+            assert torch.equal(out[k], base[k]), k
+        for (a, _), (b, _) in zip(norms, base_norms):
+            assert abs(a - b) <= 1e-5 * b
+
+
+def test_subnormals_kept():
+    """Tiny gradients drive v into the FP32 subnormal range and tiny weights give fp16
+    subnormal half copies; both must match the oracle (no flush to zero)."""
+    w = _custom("subnormal", [4096], [True])
+    w.grad_sigma = 1e-21
+    w.master_sigma = 1e-6
+    w.hyper.init_scale = 2.0 ** 60
+    log("case subnormals")
+    run_sequence(w, 3, clip_norm=0.0, where=" subnormal")
+
+
+def test_overflow_from_unscale_factor():
+    """bf16 gradients with a scale below one: finite gradients whose FP32 unscaled
+    value overflows must skip, exactly as the oracle decides in FP32."""
+    w = _custom("bf16_big", [1000], [True], W.BF16, scaler_mode=W.DYNAMIC,
+                init_scale=2.0 ** -10, min_scale=2.0 ** -20)
+    shard = DeviceShard(w)
+    shard.init_()
+    chk = Checker(shard)
+    try:
+        big = torch.full((1000,), 2.0 ** 120, dtype=torch.bfloat16, device="cuda")
+        shard.segs[0]["grad"].copy_(big)
+        gst, d = chk.step(1e-3, where=" overflow")
+        assert d.skip == 1 and gst.loss_scale == 2.0 ** -11
+        W.device_grads_(w, shard.segs[0]["grad"], 1, 1.0)
+        gst, d = chk.step(1e-3, where=" clean")
+        assert d.skip == 0
+    finally:
+        chk.close()
+
+
+def test_resume_equals_continuous():
+    """N steps, destroy, re-create with the state read back, M steps == N+M steps."""
+    w = _custom("resume", [30_000, 2048], [True, False], growth_interval=2)
+    w.injections = {1: [(5, "nan")]}
+    a = DeviceShard(w)
+    a.init_()
+    ha = Z.neox_zero1_create(lib_config(w), a.neox_segments(), 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    for k in range(6):
+        a.grads_(k, Z.neox_scaler_state(ha).loss_scale)
+        Z.neox_zero1_step(ha, 1e-3, stream)
+    ref = Z.neox_scaler_state(ha)
+    Z.neox_zero1_destroy(ha)
+
+    b = DeviceShard(w)
+    b.init_()
+    hb = Z.neox_zero1_create(lib_config(w), b.neox_segments(), 0)
+    for k in range(3):
+        b.grads_(k, Z.neox_scaler_state(hb).loss_scale)
+        Z.neox_zero1_step(hb, 1e-3, stream)
+    st = Z.neox_scaler_state(hb)
+    Z.neox_zero1_destroy(hb)
+    hb = Z.neox_zero1_create(
+        lib_config(w, init_scale=st.loss_scale, init_step=st.step, init_skipped=st.skipped_total,
+                   init_good_steps=st.good_steps,
+                   init_consecutive_overflows=st.consecutive_overflows),
+        b.neox_segments(), 0)
+    for k in range(3, 6):
+        b.grads_(k, Z.neox_scaler_state(hb).loss_scale)
+        Z.neox_zero1_step(hb, 1e-3, stream)
+    st2 = Z.neox_scaler_state(hb)
+    Z.neox_zero1_destroy(hb)
+    assert (st2.loss_scale, st2.step, st2.skipped_total, st2.good_steps) == \
+        (ref.loss_scale, ref.step, ref.skipped_total, ref.good_steps)
+    oa, ob = _outputs(a), _outputs(b)
+    for k in oa:
+        assert torch.equal(oa[k], ob[k]), k
