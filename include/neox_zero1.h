@@ -81,7 +81,8 @@ typedef struct neox_zero1_config {
     /* Launch shape; 0 selects the default.  Results other than the norm's last bits
      * do not depend on either. */
     uint32_t chunk_elems;          /* elements per work chunk: multiple of 8, 256..2^24 */
-    uint32_t norm_blocks;          /* blocks of the norm pass                           */
+    uint32_t norm_blocks;          /* norm pass grid: 0 = one block per chunk, else this
+                                      many blocks striding over the chunks              */
 } neox_zero1_config;
 
 /* One contiguous run of parameters of the shard, with its five device arrays, each

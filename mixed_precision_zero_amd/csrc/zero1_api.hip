@@ -33,8 +33,17 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(NEOX_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-constexpr uint32_t kDefaultChunk = 8192;
-constexpr uint32_t kNormBlocksPerCU = 8;
+// Work-unit sizes (elements), measured best on MI355X: the update wants small blocks
+// (one 16-byte vector per array per thread and pass), the read-only norm pass wants
+// more bytes per block.
+#ifndef NZ1_UPDATE_CHUNK
+#define NZ1_UPDATE_CHUNK 4096
+#endif
+#ifndef NZ1_NORM_CHUNK
+#define NZ1_NORM_CHUNK 16384
+#endif
+constexpr uint32_t kDefaultChunk = NZ1_UPDATE_CHUNK;
+constexpr uint32_t kNormChunk = NZ1_NORM_CHUNK;
 
 struct TimingSlot {
     hipEvent_t ev[4];
@@ -45,9 +54,11 @@ struct TimingSlot {
 struct neox_zero1 {
     neox_zero1_config cfg;
     int device = 0;
-    uint32_t nchunks = 0;
+    uint32_t nchunks = 0;          // update work units
+    uint32_t nnorm = 0;            // norm-pass work units
     uint32_t norm_blocks = 0;
     Chunk* d_chunks = nullptr;
+    Chunk* d_norm_chunks = nullptr;
     double* d_partial = nullptr;
     DevState* d_state = nullptr;
     hipStream_t last_stream = nullptr;
@@ -261,6 +272,7 @@ static void free_handle(neox_zero1* h) {
         for (auto& e : s.ev)
             if (e) (void)hipEventDestroy(e);
     if (h->d_chunks) (void)hipFree(h->d_chunks);
+    if (h->d_norm_chunks) (void)hipFree(h->d_norm_chunks);
     if (h->d_partial) (void)hipFree(h->d_partial);
     if (h->d_state) (void)hipFree(h->d_state);
     delete h;
@@ -276,10 +288,15 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     rc = validate_segments(segs, nseg);
     if (rc) return rc;
 
+    // update chunks of C elements; norm chunks of the smallest multiple of C that is
+    // at least kNormChunk
     const uint32_t C = cfg->chunk_elems ? cfg->chunk_elems : kDefaultChunk;
-    std::vector<Chunk> table;
+    const uint64_t C1_64 = C >= kNormChunk ? C : (uint64_t)(kNormChunk + C - 1) / C * C;
+    const uint32_t C1 = C1_64 > (1u << 24) ? C : (uint32_t)C1_64;
+    std::vector<Chunk> table, norm_table;
     try {
         build_chunks(segs, nseg, C, table);
+        build_chunks(segs, nseg, C1, norm_table);
     } catch (const std::bad_alloc&) {
         return fail(NEOX_ENOMEM, "host allocation of the chunk table");
     }
@@ -293,15 +310,15 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) { free_handle(h); return hip_fail(e, "hipGetDevice"); }
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
-    if (e != hipSuccess) { free_handle(h); return hip_fail(e, "hipDeviceGetAttribute"); }
-    uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : (uint32_t)cus * kNormBlocksPerCU;
-    if (nb > h->nchunks) nb = h->nchunks;
+    h->nnorm = (uint32_t)norm_table.size();
+    // norm pass: one block per norm chunk unless a smaller striding grid is requested
+    uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : h->nnorm;
+    if (nb > h->nnorm) nb = h->nnorm;
     if (nb == 0) nb = 1;
     h->norm_blocks = nb;
 
     e = hipMalloc(&h->d_chunks, table.size() * sizeof(Chunk));
+    if (e == hipSuccess) e = hipMalloc(&h->d_norm_chunks, norm_table.size() * sizeof(Chunk));
     if (e == hipSuccess) e = hipMalloc(&h->d_partial, nb * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_state, sizeof(DevState));
     if (e != hipSuccess) {
@@ -324,6 +341,9 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     st.skip = 1;
 
     e = hipMemcpyAsync(h->d_chunks, table.data(), table.size() * sizeof(Chunk), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h->d_norm_chunks, norm_table.data(), norm_table.size() * sizeof(Chunk),
+                           hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(h->d_state, &st, sizeof st, hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) { free_handle(h); return hip_fail(e, "upload of the chunk table"); }
@@ -366,7 +386,7 @@ extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
     hipError_t e = hipSuccess;
     if (ts) e = hipEventRecord(ts->ev[0], stream);
     if (e == hipSuccess)
-        e = launch_norm(h->cfg.dtype, h->d_chunks, h->nchunks, h->norm_blocks, h->d_state,
+        e = launch_norm(h->cfg.dtype, h->d_norm_chunks, h->nnorm, h->norm_blocks, h->d_state,
                         h->d_partial, stream);
     if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[1], stream);
     if (e == hipSuccess) e = launch_finalize(h->d_partial, h->norm_blocks, h->d_state, h->fin, stream);

@@ -1,11 +1,12 @@
 // zero1_kernels.hip -- gfx950 kernels of the ZeRO-1 mixed-precision Adam step.
 //
 // Three launches per step, all on the caller's stream:
-//   norm      persistent grid; every block walks a fixed, strided set of chunks and
-//             accumulates the squares of the unscaled FP32 gradient in double.  A
-//             non-finite unscaled value makes its square, and so the block's sum,
-//             non-finite; finite values cannot overflow a double sum (|g| < 2^128 so
-//             g^2 < 2^256), so "sum not finite" is exactly "some gradient overflowed".
+//   norm      one block per chunk (or a smaller grid striding over the chunks);
+//             each block sums the squares of its unscaled FP32 gradient in double and
+//             writes one partial.  A non-finite unscaled value makes its square, and so
+//             the sum, non-finite; finite values cannot overflow a double sum (|g| <
+//             2^128 so g^2 < 2^256), so "sum not finite" is exactly "some gradient
+//             overflowed".
 //   finalize  one block; fixed-order sum of the per-block partials, then the skip
 //             decision, clip coefficient, step count, bias corrections and the loss
 //             scale update, written to the device state block.
@@ -66,18 +67,69 @@ struct Fmt<2> {
 };
 
 // ------------------------------------------------------------------------------------
+// 16-byte global accesses, optionally non-temporal (streamed data is touched once).
+// Compile-time tuning knobs; the defaults are the measured best on MI355X.
+// ------------------------------------------------------------------------------------
+#ifndef NZ1_NORM_NT_LOAD
+#define NZ1_NORM_NT_LOAD 1
+#endif
+#ifndef NZ1_UPDATE_NT_LOAD
+#define NZ1_UPDATE_NT_LOAD 0
+#endif
+#ifndef NZ1_UPDATE_NT_STORE
+#define NZ1_UPDATE_NT_STORE 0
+#endif
+#ifndef NZ1_UPDATE_UNROLL
+#define NZ1_UPDATE_UNROLL 2
+#endif
+#ifndef NZ1_UPDATE_REVERSE
+#define NZ1_UPDATE_REVERSE 1
+#endif
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint4* p) {
+    u32x4 r;
+    if constexpr (NT) r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else r = *reinterpret_cast<const u32x4*>(p);
+    return make_uint4(r.x, r.y, r.z, r.w);
+}
+template <bool NT>
+__device__ __forceinline__ float4 ld16(const float4* p) {
+    f32x4 r;
+    if constexpr (NT) r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    else r = *reinterpret_cast<const f32x4*>(p);
+    return make_float4(r.x, r.y, r.z, r.w);
+}
+template <bool NT>
+__device__ __forceinline__ void st16(uint4* p, uint4 v) {
+    const u32x4 r = {v.x, v.y, v.z, v.w};
+    if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = r;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(float4* p, float4 v) {
+    const f32x4 r = {v.x, v.y, v.z, v.w};
+    if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = r;
+}
+
+// ------------------------------------------------------------------------------------
 // Deterministic block reduction of a double: xor-butterfly inside each wave64 (every
 // lane ends with the same, order-fixed value), then wave 0..3 partials in index order.
 // ------------------------------------------------------------------------------------
+template <int NT>
 __device__ __forceinline__ double block_sum(double v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    __shared__ double ws[kBlock / 64];
+    __shared__ double ws[NT / 64];
     if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
     __syncthreads();
     double r = ws[0];
 #pragma unroll
-    for (int k = 1; k < kBlock / 64; ++k) r += ws[k];
+    for (int k = 1; k < NT / 64; ++k) r += ws[k];
     return r;
 }
 
@@ -113,16 +165,16 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ 
             const uint32_t nvec = len / kVec;
             uint32_t i = threadIdx.x;
             for (; i + 3 * kBlock < nvec; i += 4 * kBlock) {
-                const uint4 q0 = g4[i];
-                const uint4 q1 = g4[i + kBlock];
-                const uint4 q2 = g4[i + 2 * kBlock];
-                const uint4 q3 = g4[i + 3 * kBlock];
+                const uint4 q0 = ld16<NZ1_NORM_NT_LOAD>(g4 + i);
+                const uint4 q1 = ld16<NZ1_NORM_NT_LOAD>(g4 + i + kBlock);
+                const uint4 q2 = ld16<NZ1_NORM_NT_LOAD>(g4 + i + 2 * kBlock);
+                const uint4 q3 = ld16<NZ1_NORM_NT_LOAD>(g4 + i + 3 * kBlock);
                 sq8<DT>(q0, inv, a0, a1);
                 sq8<DT>(q1, inv, a0, a1);
                 sq8<DT>(q2, inv, a0, a1);
                 sq8<DT>(q3, inv, a0, a1);
             }
-            for (; i < nvec; i += kBlock) sq8<DT>(g4[i], inv, a0, a1);
+            for (; i < nvec; i += kBlock) sq8<DT>(ld16<NZ1_NORM_NT_LOAD>(g4 + i), inv, a0, a1);
             done = nvec * kVec;
         }
         for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
@@ -130,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ 
             a0 = __builtin_fma(x, x, a0);
         }
     }
-    const double s = block_sum(a0 + a1);
+    const double s = block_sum<kBlock>(a0 + a1);
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
@@ -144,13 +196,26 @@ __device__ __forceinline__ bool f32_finite(float x) {
     return (__float_as_uint(x) & 0x7F800000u) != 0x7F800000u;
 }
 
-__global__ __launch_bounds__(kBlock) void finalize_kernel(const double* __restrict__ partial,
-                                                          uint32_t nparts,
-                                                          DevState* __restrict__ st,
-                                                          FinalizeArgs a) {
+constexpr int kFinalizeBlock = 1024;
+
+__global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* __restrict__ partial,
+                                                                  uint32_t nparts,
+                                                                  DevState* __restrict__ st,
+                                                                  FinalizeArgs a) {
+    // fixed order: thread t owns partials t, t + 1024, ...; four independent loads per
+    // round keep the (one-block) read of up to a few MB of partials latency-tolerant
     double acc = 0.0;
-    for (uint32_t i = threadIdx.x; i < nparts; i += kBlock) acc += partial[i];
-    const double sumsq = block_sum(acc);
+    uint32_t i = threadIdx.x;
+    for (; i + 3 * kFinalizeBlock < nparts; i += 4 * kFinalizeBlock) {
+        const double p0 = partial[i], p1 = partial[i + kFinalizeBlock];
+        const double p2 = partial[i + 2 * kFinalizeBlock], p3 = partial[i + 3 * kFinalizeBlock];
+        acc += p0;
+        acc += p1;
+        acc += p2;
+        acc += p3;
+    }
+    for (; i < nparts; i += kFinalizeBlock) acc += partial[i];
+    const double sumsq = block_sum<kFinalizeBlock>(acc);
     if (threadIdx.x != 0) return;
 
     float scale = st->loss_scale;
@@ -221,7 +286,9 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
                                                         const DevState* __restrict__ st,
                                                         UpdateArgs a) {
     if (st->skip) return;
-    const Chunk* ch = chunks + blockIdx.x;
+    // NZ1_UPDATE_REVERSE walks the chunks last-to-first, so the first gradients the
+    // update reads are the ones the norm pass read last
+    const Chunk* ch = chunks + (NZ1_UPDATE_REVERSE ? gridDim.x - 1 - blockIdx.x : blockIdx.x);
     const uint32_t len = ch->len;
     const uint32_t flags = ch->flags;
     const bool decay = (flags & CH_DECAY) != 0;
@@ -247,13 +314,13 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = base + u * kBlock + threadIdx.x;
                 if (i < nvec) {
-                    G[u] = g4[i];
-                    W[u][0] = w4[2 * i];
-                    W[u][1] = w4[2 * i + 1];
-                    M[u][0] = m4[2 * i];
-                    M[u][1] = m4[2 * i + 1];
-                    V[u][0] = v4[2 * i];
-                    V[u][1] = v4[2 * i + 1];
+                    G[u] = ld16<NZ1_UPDATE_NT_LOAD>(g4 + i);
+                    W[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(w4 + 2 * i);
+                    W[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(w4 + 2 * i + 1);
+                    M[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(m4 + 2 * i);
+                    M[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(m4 + 2 * i + 1);
+                    V[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i);
+                    V[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i + 1);
                 }
             }
 #pragma unroll
@@ -273,14 +340,15 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
                         adam(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], v[2 * k + 1], c, a,
                              decay);
                     }
-                    w4[2 * i] = make_float4(w[0], w[1], w[2], w[3]);
-                    w4[2 * i + 1] = make_float4(w[4], w[5], w[6], w[7]);
-                    m4[2 * i] = make_float4(m[0], m[1], m[2], m[3]);
-                    m4[2 * i + 1] = make_float4(m[4], m[5], m[6], m[7]);
-                    v4[2 * i] = make_float4(v[0], v[1], v[2], v[3]);
-                    v4[2 * i + 1] = make_float4(v[4], v[5], v[6], v[7]);
-                    h4[i] = make_uint4(Fmt<DT>::pack(w[0], w[1]), Fmt<DT>::pack(w[2], w[3]),
-                                       Fmt<DT>::pack(w[4], w[5]), Fmt<DT>::pack(w[6], w[7]));
+                    constexpr bool NTS = NZ1_UPDATE_NT_STORE;
+                    st16<NTS>(w4 + 2 * i, make_float4(w[0], w[1], w[2], w[3]));
+                    st16<NTS>(w4 + 2 * i + 1, make_float4(w[4], w[5], w[6], w[7]));
+                    st16<NTS>(m4 + 2 * i, make_float4(m[0], m[1], m[2], m[3]));
+                    st16<NTS>(m4 + 2 * i + 1, make_float4(m[4], m[5], m[6], m[7]));
+                    st16<NTS>(v4 + 2 * i, make_float4(v[0], v[1], v[2], v[3]));
+                    st16<NTS>(v4 + 2 * i + 1, make_float4(v[4], v[5], v[6], v[7]));
+                    st16<NTS>(h4 + i, make_uint4(Fmt<DT>::pack(w[0], w[1]), Fmt<DT>::pack(w[2], w[3]),
+                                                 Fmt<DT>::pack(w[4], w[5]), Fmt<DT>::pack(w[6], w[7])));
                 }
             }
         }
@@ -300,7 +368,7 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
-constexpr int kUpdateUnroll = 2;
+constexpr int kUpdateUnroll = NZ1_UPDATE_UNROLL;
 
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
                        const DevState* st, double* partial, hipStream_t stream) {
@@ -313,7 +381,7 @@ hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_
 
 hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
                            const FinalizeArgs& a, hipStream_t stream) {
-    finalize_kernel<<<1, kBlock, 0, stream>>>(partial, nparts, st, a);
+    finalize_kernel<<<1, kFinalizeBlock, 0, stream>>>(partial, nparts, st, a);
     return hipGetLastError();
 }
 
