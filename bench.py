@@ -45,10 +45,92 @@ def read_traffic(workload, n):
     try:
         if vals.get("kernel_source_sha256") != kernel_sha() or vals.get("workload") != workload:
             return None
-        kib = float(vals["fetch_kib_per_dispatch"]) + float(vals["write_kib_per_dispatch"])
-        return kib * 1024.0 * float(vals["copy_factor"])
+        return 1024.0 * (float(vals["fetch_kib_per_dispatch"]) * float(vals["copy_factor_fetch"])
+                         + float(vals["write_kib_per_dispatch"]) * float(vals["copy_factor_write"]))
     except (KeyError, ValueError):
         return None
+
+
+def summarize_pmc(args):
+    """Write the traffic summary bench.py reads (profiles/...) from rocprofv3 --pmc
+    output: FETCH_SIZE and WRITE_SIZE of the update kernel, each scaled by what the same
+    counter reads for a plain streaming copy of known size (--copy-probe-only run)."""
+    import csv
+    import glob
+
+    def rows(d):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        if not out:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        return out
+
+    def avg(d, counter, name_part):
+        vals = [float(r["Counter_Value"]) for r in rows(d)
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} in {d}")
+        return sum(vals) / len(vals), len(vals)
+
+    fetch, nf = avg(args.pmc_fetch, "FETCH_SIZE", "update_kernel")
+    write, nw = avg(args.pmc_write, "WRITE_SIZE", "update_kernel")
+    cfetch, _ = avg(args.pmc_copy_fetch, "FETCH_SIZE", "MulFunctor")
+    cwrite, _ = avg(args.pmc_copy_write, "WRITE_SIZE", "MulFunctor")
+    known_kib = args.copy_bytes / 1024.0
+    ff, fw = known_kib / cfetch, known_kib / cwrite
+    import workloads as W
+    n = W.BENCH_WORKLOADS[args.workload]().numel
+    traffic = (fetch * ff + write * fw) * 1024.0
+    lines = [
+        f"# HBM traffic of the update kernel on {args.workload} ({n} params), from rocprofv3 PMC.",
+        "# Commands (run from the repository root on the MI355X box):",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- python3 bench.py "
+        f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <write_dir> ... (same program)",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch_dir> --output-format csv -- python3 bench.py "
+        f"--copy-probe-only {args.copy_bytes}",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <copy_write_dir> ... (same program)",
+        f"#   python3 bench.py --summarize-pmc --workload {args.workload} --copy-bytes "
+        f"{args.copy_bytes} --pmc-fetch <fetch_dir> --pmc-write <write_dir> "
+        "--pmc-copy-fetch <copy_fetch_dir> --pmc-copy-write <copy_write_dir>",
+        "# The copy probe reads and writes copy_bytes once per dispatch; its counter readings",
+        "# give the factors that turn counter KiB into bytes.  Counters count traffic leaving",
+        "# the L2 (Infinity Cache hits included).",
+        f"workload: {args.workload}",
+        f"kernel_source_sha256: {kernel_sha()}",
+        f"update_dispatches: {nf}",
+        f"fetch_kib_per_dispatch: {fetch:.1f}",
+        f"write_kib_per_dispatch: {write:.1f}",
+        f"copy_bytes: {args.copy_bytes}",
+        f"copy_fetch_kib_per_dispatch: {cfetch:.1f}",
+        f"copy_write_kib_per_dispatch: {cwrite:.1f}",
+        f"copy_factor_fetch: {ff:.5f}",
+        f"copy_factor_write: {fw:.5f}",
+        f"traffic_bytes_per_dispatch: {traffic:.0f}",
+        f"algorithmic_bytes_per_dispatch: {UPDATE_BYTES_PER_PARAM * n}",
+        f"traffic_over_algorithmic: {traffic / (UPDATE_BYTES_PER_PARAM * n):.4f}",
+    ]
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text, end="")
+
+
+def copy_probe(nbytes):
+    """A plain streaming copy of known size for counter calibration: reads and writes
+    nbytes once per dispatch, three dispatches."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: 3 x {nbytes} bytes", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
@@ -100,7 +182,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing-events", action="store_true",
                     help="time whole steps only (no per-kernel events)")
+    ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
+                    help="run only a plain streaming copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-pmc", action="store_true",
+                    help="write the update kernel's traffic summary from rocprofv3 --pmc runs")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--pmc-copy-fetch")
+    ap.add_argument("--pmc-copy-write")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--out")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.copy_probe_only:
+        copy_probe(args.copy_probe_only)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the step is per-rank work and multi-GPU runs are not part of it", file=sys.stderr)
