@@ -133,6 +133,32 @@ def copy_probe(nbytes):
     print(f"[bench] copy probe: 3 x {nbytes} bytes", file=sys.stderr, flush=True)
 
 
+def measure_ceiling(bufs, n, reps=20):
+    """GB/s of the stream probes on the workload's own arrays (contents are clobbered)."""
+    import torch
+
+    from mixed_precision_zero_amd import probe as P
+    stream = torch.cuda.current_stream()
+    ptr = {k: t.data_ptr() for k, t in bufs.items()}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_pat = timed(lambda: P.neox_probe_update_pattern(ptr["grad"], ptr["half"], ptr["master"],
+                                                       ptr["m"], ptr["v"], n, stream.cuda_stream))
+    ms_copy = timed(lambda: P.neox_probe_copy(ptr["master"], ptr["m"], 4 * n, stream.cuda_stream))
+    return {"update_pattern_gbps": UPDATE_BYTES_PER_PARAM * n / (ms_pat * 1e-3) / 1e9,
+            "copy_gbps": 8 * n / (ms_copy * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
     """The oracle as it stands, one thread, on the first `sample` params of the shard."""
     import numpy as np
@@ -180,6 +206,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="neox20b_shard_215m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the attainable-bandwidth probes after the timed steps")
     ap.add_argument("--no-timing-events", action="store_true",
                     help="time whole steps only (no per-kernel events)")
     ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
@@ -276,6 +304,7 @@ def main():
         kernel_ms = [s / k for s in sums]
     Z.neox_zero1_destroy(h)
     assert st.skipped_total == 0 and st.step == args.warmup + args.steps, "bench steps were skipped"
+    ceiling = measure_ceiling(keep[0], n) if w.flat and n % 8 == 0 and not args.no_ceiling else None
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = n / (ms_per_step * 1e-3)
@@ -309,6 +338,14 @@ def main():
                            "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n}
         out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],
                                 "update": kernel_ms[2]}
+    if ceiling:
+        ceiling["note"] = ("measured on this GPU right after the timed steps: a kernel with the "
+                           "update's exact access pattern and trivial arithmetic, and a plain copy")
+        if kernel_ms:
+            ceiling["update_kernel_frac_of_pattern"] = out["roofline"]["achieved"] / \
+                ceiling["update_pattern_gbps"]
+        ceiling["step_frac_of_pattern"] = out["hbm"]["step_gbps"] / ceiling["update_pattern_gbps"]
+        out["ceiling"] = ceiling
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, one thread)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -6,6 +6,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SO = os.path.join(PKG, "libneox_zero1.so")
 SOURCES = [os.path.join(PKG, "csrc", f) for f in ("zero1_kernels.hip", "zero1_api.hip")]
+PROBE_SO = os.path.join(PKG, "libneox_stream_probe.so")
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "stream_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -17,16 +19,21 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = SO + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _hipcc(sources, out, verbose):
+    tmp = out + ".tmp"
+    res = subprocess.run([HIPCC, *FLAGS, *sources, "-o", tmp], capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(res.stderr)
-    os.replace(tmp, SO)
-    return SO
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """The step library, and the bandwidth-probe library the benchmark uses."""
+    _hipcc(PROBE_SOURCES, PROBE_SO, verbose)
+    return _hipcc(SOURCES, SO, verbose)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,97 @@
+// stream_probe.hip -- attainable-bandwidth probes for the benchmark (see
+// include/neox_stream_probe.h).  They share no code with the step's kernels on purpose:
+// each is a self-contained restatement of an access pattern.
+#include "neox_stream_probe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+int fail(int code, const char* msg) {
+    g_err = msg;
+    return code;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, uint64_t nvec) {
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < nvec) dst[i] = src[i];
+}
+
+// 4096-element blocks walked last-to-first, two 8-element vectors per thread: the
+// update kernel's tiling, with its arithmetic replaced by a few multiplies.
+constexpr uint32_t kTile = 4096;
+
+__global__ __launch_bounds__(256) void pattern_kernel(const u32x4* __restrict__ g,
+                                                      u32x4* __restrict__ h,
+                                                      f32x4* __restrict__ w,
+                                                      f32x4* __restrict__ m,
+                                                      f32x4* __restrict__ v, uint64_t nvec) {
+    const uint64_t tile = gridDim.x - 1 - blockIdx.x;
+    const uint64_t base = tile * (kTile / 8);
+    u32x4 G[2];
+    f32x4 W[2][2], M[2][2], V[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint64_t i = base + u * 256 + threadIdx.x;
+        if (i < nvec) {
+            G[u] = g[i];
+            W[u][0] = w[2 * i]; W[u][1] = w[2 * i + 1];
+            M[u][0] = m[2 * i]; M[u][1] = m[2 * i + 1];
+            V[u][0] = v[2 * i]; V[u][1] = v[2 * i + 1];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint64_t i = base + u * 256 + threadIdx.x;
+        if (i < nvec) {
+            const float gs = __uint_as_float(G[u].x << 16) * 1e-30f;
+            w[2 * i] = W[u][0] + gs; w[2 * i + 1] = W[u][1] + gs;
+            m[2 * i] = M[u][0] * 0.9f; m[2 * i + 1] = M[u][1] * 0.9f;
+            v[2 * i] = V[u][0] * 0.95f; v[2 * i + 1] = V[u][1] * 0.95f;
+            const u32x4 hh = {__float_as_uint(W[u][0].x) >> 16, __float_as_uint(W[u][0].z) >> 16,
+                              __float_as_uint(W[u][1].x) >> 16, __float_as_uint(W[u][1].z) >> 16};
+            h[i] = hh;
+        }
+    }
+}
+
+bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int neox_probe_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream) {
+    if (!src || !dst || bytes == 0 || bytes % 16 || !a16(src) || !a16(dst))
+        return fail(-1, "copy probe: null, unaligned or bad size");
+    const uint64_t nvec = bytes / 16;
+    const uint64_t grid = (nvec + 255) / 256;
+    if (grid > 0xFFFFFFFFull / 256) return fail(-1, "copy probe: too large");
+    copy_kernel<<<(uint32_t)grid, 256, 0, (hipStream_t)hip_stream>>>(
+        (const u32x4*)src, (u32x4*)dst, nvec);
+    return hipGetLastError() == hipSuccess ? 0 : fail(-2, "copy probe launch failed");
+}
+
+extern "C" int neox_probe_update_pattern(const void* grad, void* half, float* master,
+                                         float* exp_avg, float* exp_avg_sq, uint64_t n,
+                                         void* hip_stream) {
+    if (!grad || !half || !master || !exp_avg || !exp_avg_sq || n == 0 || n % 8)
+        return fail(-1, "pattern probe: null or n not a positive multiple of 8");
+    if (!a16(grad) || !a16(half) || !a16(master) || !a16(exp_avg) || !a16(exp_avg_sq))
+        return fail(-1, "pattern probe: arrays must be 16-byte aligned");
+    const uint64_t tiles = (n + kTile - 1) / kTile;
+    if (tiles > 0xFFFFFFFFull / 256) return fail(-1, "pattern probe: too large");
+    pattern_kernel<<<(uint32_t)tiles, 256, 0, (hipStream_t)hip_stream>>>(
+        (const u32x4*)grad, (u32x4*)half, (f32x4*)master, (f32x4*)exp_avg, (f32x4*)exp_avg_sq,
+        n / 8);
+    return hipGetLastError() == hipSuccess ? 0 : fail(-2, "pattern probe launch failed");
+}
+
+extern "C" const char* neox_probe_last_error(void) { return g_err.c_str(); }

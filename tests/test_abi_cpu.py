@@ -31,6 +31,24 @@ def test_library_exports_every_declared_symbol():
     assert sorted(Z.EXPORTS) == syms
 
 
+def test_probe_library_exports_every_declared_symbol():
+    from mixed_precision_zero_amd import probe as P
+    text = open(os.path.join(ROOT, "include", "neox_stream_probe.h")).read()
+    syms = sorted(set(re.findall(r"^(?:int|const char\*)\s+(neox_\w+)\s*\(", text, re.M)))
+    assert sorted(P.EXPORTS) == syms
+    L = C.CDLL(P.LIB_PATH)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_probe_rejects_bad_arguments():
+    from mixed_precision_zero_amd import probe as P
+    with pytest.raises(RuntimeError):
+        P.neox_probe_copy(0, 0, 16)
+    with pytest.raises(RuntimeError):
+        P.neox_probe_update_pattern(16, 16, 16, 16, 16, 7)
+
+
 def test_default_config():
     cfg = Z.neox_zero1_default_config()
     assert (cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.clip_norm) == (0.9, 0.95, 1e-8, 0.01, 1.0)
