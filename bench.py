@@ -179,7 +179,8 @@ def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
                    clip_norm=h.clip_norm, predivide_factor=h.predivide_factor,
                    dp_world_size=h.dp_world_size, dtype=h.dtype, scaler_mode=h.scaler_mode,
                    growth_interval=h.growth_interval, growth_factor=h.growth_factor,
-                   backoff_factor=h.backoff_factor, min_scale=h.min_scale)
+                   backoff_factor=h.backoff_factor, min_scale=h.min_scale,
+                   optimizer=h.optimizer)
     st = O.Scaler(loss_scale=h.init_scale)
     spent, steps = 0.0, 0
     while spent < budget_s and steps < 50:
@@ -188,7 +189,7 @@ def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
         for n, d in segs:
             sl = slice(off, off + n)
             osegs.append(dict(grad=g[sl], half=st0["half"][sl], master=st0["master"][sl],
-                              m=st0["m"][sl], v=st0["v"][sl], decay=d))
+                              m=st0["m"][sl], v=None if h.optimizer else st0["v"][sl], decay=d))
             off += n
         t0 = time.perf_counter()
         O.step(cfg, st, np.float32(h.lr), osegs)
@@ -208,6 +209,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the attainable-bandwidth probes after the timed steps")
+    ap.add_argument("--optimizer", choices=("adamw", "sgd"), default="adamw",
+                    help="sgd: momentum SGD on the same shard (no second moment)")
+    ap.add_argument("--split", action="store_true",
+                    help="time the split step (step_local + step_apply on the local value)")
+    ap.add_argument("--segment-norms", action="store_true",
+                    help="keep per-segment squared norms (telemetry) during the step")
     ap.add_argument("--no-timing-events", action="store_true",
                     help="time whole steps only (no per-kernel events)")
     ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
@@ -240,7 +247,11 @@ def main():
     if args.workload not in W.BENCH_WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; one of {sorted(W.BENCH_WORKLOADS)}")
     w = W.BENCH_WORKLOADS[args.workload]()
+    sgd = args.optimizer == "sgd"
+    w.hyper.optimizer = 1 if sgd else 0
     n = w.numel
+    upd_bpp = 20 if sgd else UPDATE_BYTES_PER_PARAM     # SGD: no second moment to move
+    step_bpp = upd_bpp + 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     dt = torch.float16 if w.hyper.dtype == W.F16 else torch.bfloat16
@@ -249,25 +260,27 @@ def main():
 
     keep = []
     segs = []
+    kinds = [("grad", dt), ("half", dt), ("master", torch.float32), ("m", torch.float32)]
+    if not sgd:
+        kinds.append(("v", torch.float32))
     if w.flat:
-        bufs = {k: torch.empty(n, dtype=t, device=dev) for k, t in
-                (("grad", dt), ("half", dt), ("master", torch.float32), ("m", torch.float32),
-                 ("v", torch.float32))}
+        bufs = {k: torch.empty(n, dtype=t, device=dev) for k, t in kinds}
+        bufs.setdefault("v", None)
         W.device_init_(w, bufs["master"], bufs["half"], bufs["m"], bufs["v"])
         W.device_grads_(w, bufs["grad"], 0, w.hyper.init_scale)
         off = 0
         for numel, decay in w.segments:
             sl = slice(off, off + numel)
-            segs.append(Z.segment(*(bufs[k][sl] for k in ("grad", "half", "master", "m", "v")),
-                                  decay))
+            v = None if sgd else bufs["v"][sl]
+            segs.append(Z.segment(bufs["grad"][sl], bufs["half"][sl], bufs["master"][sl],
+                                  bufs["m"][sl], v, decay))
             off += numel
         keep.append(bufs)
     else:
         off = 0
         for i, (numel, decay) in enumerate(w.segments):
-            a = {k: torch.empty(numel, dtype=t, device=dev) for k, t in
-                 (("grad", dt), ("half", dt), ("master", torch.float32), ("m", torch.float32),
-                  ("v", torch.float32))}
+            a = {k: torch.empty(numel, dtype=t, device=dev) for k, t in kinds}
+            a.setdefault("v", None)
             W.device_init_(w, a["master"], a["half"], a["m"], a["v"], i + 1)
             W.device_grads_(w, a["grad"], 0, w.hyper.init_scale, off)
             segs.append(Z.segment(a["grad"], a["half"], a["master"], a["m"], a["v"], decay))
@@ -280,31 +293,50 @@ def main():
         predivide_factor=w.hyper.predivide_factor, dp_world_size=w.hyper.dp_world_size,
         dtype=w.hyper.dtype, scaler_mode=w.hyper.scaler_mode,
         growth_interval=w.hyper.growth_interval, init_scale=w.hyper.init_scale,
-        min_scale=w.hyper.min_scale), segs, stream.cuda_stream)
+        min_scale=w.hyper.min_scale, optimizer=w.hyper.optimizer,
+        segment_norms=int(args.segment_norms)), segs, stream.cuda_stream)
+    loc = torch.zeros(1, dtype=torch.float64, device=dev)
+
+    def one_step():
+        if args.split:
+            # one rank: the exchange of the local norm is the identity
+            Z.neox_zero1_step_local(h, loc.data_ptr(), stream.cuda_stream)
+            Z.neox_zero1_step_apply(h, loc.data_ptr(), w.hyper.lr, stream.cuda_stream)
+        else:
+            Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
 
     for _ in range(args.warmup):
-        Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
+        one_step()
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
           flush=True)
 
-    timed_events = not args.no_timing_events
+    # The timed steps record only the update kernel's two events; the norm / finalize
+    # split comes from a short pass with all events after the timed region.
+    timed_events = not args.no_timing_events and not args.split
     if timed_events:
-        Z.neox_zero1_timing_begin(h, args.steps)
+        Z.neox_zero1_timing_begin(h, args.steps, update_only=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
+        one_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st = Z.neox_scaler_state(h)
     kernel_ms = None
     if timed_events:
         sums, k = Z.neox_zero1_timing_end(h)
-        kernel_ms = [s / k for s in sums]
+        update_ms = sums[2] / k
+        nb = min(20, args.steps)
+        Z.neox_zero1_timing_begin(h, nb)
+        for _ in range(nb):
+            one_step()
+        sums, k2 = Z.neox_zero1_timing_end(h)
+        kernel_ms = [sums[0] / k2, sums[1] / k2, update_ms]
     Z.neox_zero1_destroy(h)
     assert st.skipped_total == 0 and st.step == args.warmup + args.steps, "bench steps were skipped"
-    ceiling = measure_ceiling(keep[0], n) if w.flat and n % 8 == 0 and not args.no_ceiling else None
+    ceiling = measure_ceiling(keep[0], n) if (w.flat and n % 8 == 0 and not sgd
+                                             and not args.no_ceiling) else None
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = n / (ms_per_step * 1e-3)
@@ -323,19 +355,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "params": n, "segments": len(w.segments),
                    "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
-                   "layout": "flat shard" if w.flat else "separate allocations"},
-        "hbm": {"step_bytes": STEP_BYTES_PER_PARAM * n,
-                "step_gbps": STEP_BYTES_PER_PARAM * n / (ms_per_step * 1e-3) / 1e9,
-                "step_frac_of_peak": STEP_BYTES_PER_PARAM * n / (ms_per_step * 1e-3) / 1e9
-                / HBM_PEAK_GBS},
+                   "layout": "flat shard" if w.flat else "separate allocations",
+                   "optimizer": args.optimizer, "split": args.split,
+                   "segment_norms": args.segment_norms},
+        "hbm": {"step_bytes": step_bpp * n,
+                "step_gbps": step_bpp * n / (ms_per_step * 1e-3) / 1e9,
+                "step_frac_of_peak": step_bpp * n / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     if kernel_ms:
-        upd_gbs = UPDATE_BYTES_PER_PARAM * n / (kernel_ms[2] * 1e-3) / 1e9
+        upd_gbs = upd_bpp * n / (kernel_ms[2] * 1e-3) / 1e9
+        default_mode = not (sgd or args.segment_norms)
         out["roofline"] = {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": upd_gbs / HBM_PEAK_GBS,
-                           "traffic": read_traffic(w.name, n),
+                           "traffic": read_traffic(w.name, n) if default_mode else None,
                            "kernel": "update_kernel", "avg_ms": kernel_ms[2],
-                           "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n}
+                           "bytes_per_launch": upd_bpp * n}
         out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],
                                 "update": kernel_ms[2]}
     if ceiling:

@@ -52,6 +52,9 @@ extern "C" {
 #define NEOX_SCALER_DYNAMIC 0   /* back off on overflow, grow after clean runs */
 #define NEOX_SCALER_STATIC  1   /* fixed scale; overflow still skips the step  */
 
+#define NEOX_OPT_ADAMW 0         /* Adam with bias correction, decoupled decay   */
+#define NEOX_OPT_SGD   1         /* heavy-ball momentum SGD, decoupled decay     */
+
 #define NEOX_SEG_DECAY 1u       /* segment receives decoupled weight decay      */
 #define NEOX_PAD_TENSOR 0xFFFFFFFFu
 
@@ -83,6 +86,14 @@ typedef struct neox_zero1_config {
     uint32_t chunk_elems;          /* elements per work chunk: multiple of 8, 256..2^24 */
     uint32_t norm_blocks;          /* norm pass grid: 0 = one block per chunk, else this
                                       many blocks striding over the chunks              */
+    /* Optimizer: NEOX_OPT_ADAMW, or NEOX_OPT_SGD (m = beta1*m + g; w -= lr*(m + wd*w);
+     * exp_avg holds the momentum, exp_avg_sq is unused and may be NULL).  The OPT card
+     * (方法适配) reports SGD being tried in place of Adam and reverted. */
+    int32_t  optimizer;
+    /* 1: also keep each segment's squared gradient norm of the last step on the device
+     * (neox_zero1_segment_sumsq); needs norm_blocks == 0.  Gradient-norm spikes per
+     * tensor are how the OPT card (瓶颈, 方法适配) diagnoses instability. */
+    uint32_t segment_norms;
 } neox_zero1_config;
 
 /* One contiguous run of parameters of the shard, with its five device arrays, each
@@ -184,13 +195,45 @@ int neox_scaler_state(neox_zero1* h, neox_scaler_state_t* out);
  * NULL is a no-op returning NEOX_OK. */
 int neox_zero1_destroy(neox_zero1* h);
 
-/* Per-kernel timing for profiling.  neox_zero1_timing_begin(h, max_steps) makes the
- * next max_steps steps record HIP events around each of the three kernels on their
- * stream; neox_zero1_timing_end() waits, writes the summed durations in milliseconds
- * of the norm pass, the finalize and the update to ms_sums[3] (host), the number of
- * recorded steps to *steps, and stops recording.  Errors: NEOX_EINVAL, NEOX_ENOMEM,
- * NEOX_EHIP. */
-int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps);
+/* Split step for data-parallel ranks [NeoX, 技术深度解析 parallelism table: DP + ZeRO].
+ * The clip coefficient and the skip decision need the squared norm over every rank's
+ * gradient shard, so a rank can run its step in two halves around an exchange:
+ *   neox_zero1_step_local  enqueues the norm pass and writes this rank's squared norm
+ *                          of the unscaled gradient to the device double *local_sumsq
+ *                          (non-finite if any of its unscaled values overflowed);
+ *   (caller)               sums the D ranks' values, in rank order so every rank gets
+ *                          the same bits, into a device double on each rank;
+ *   neox_zero1_step_apply  enqueues the finalize on *global_sumsq and the update.
+ * neox_zero1_step is step_local followed by step_apply on the local value.  Both
+ * return without waiting.  Errors: NEOX_EINVAL (null handle or pointer, pointer not
+ * 8-byte aligned, non-finite lr), NEOX_EHIP. */
+int neox_zero1_step_local(neox_zero1* h, double* local_sumsq, void* hip_stream);
+int neox_zero1_step_apply(neox_zero1* h, const double* global_sumsq, float lr, void* hip_stream);
+
+/* Overwrite the persistent scaler state in stream order: loss_scale, good_steps, step,
+ * skipped_total and consecutive_overflows of *st (host) replace the device copy; the
+ * last_* fields and device_loss_scale are ignored.  This is the OPT card's remedy of
+ * resetting the dynamic loss scaler or restarting from a checkpoint whose scaler is
+ * healthy (方法适配).  Errors: NEOX_EINVAL (null, loss_scale not finite and > 0, negative
+ * counters), NEOX_EHIP. */
+int neox_scaler_set(neox_zero1* h, const neox_scaler_state_t* st, void* hip_stream);
+
+/* Per-segment telemetry (handle created with segment_norms = 1): waits for the last
+ * step and writes each segment's squared norm of the unscaled gradient of that step to
+ * the host array out[nseg] (nseg = the number of segments given to create), in segment
+ * order; a non-finite value marks the segment that overflowed.  Errors: NEOX_EINVAL
+ * (null, wrong nseg, telemetry off), NEOX_EHIP. */
+int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg);
+
+/* Per-kernel timing for profiling.  neox_zero1_timing_begin(h, max_steps, update_only)
+ * makes the next max_steps calls of neox_zero1_step record HIP events on their stream:
+ * around each of the three kernels, or (update_only = 1) around the update kernel only,
+ * which keeps the recording's own cost out of the other kernels.
+ * neox_zero1_timing_end() waits, writes the summed durations in milliseconds of the
+ * norm pass, the finalize and the update to ms_sums[3] (host; the first two are 0 with
+ * update_only), the number of recorded steps to *steps, and stops recording.
+ * Errors: NEOX_EINVAL, NEOX_ENOMEM, NEOX_EHIP. */
+int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only);
 int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);
 
 /* Text of the last error raised on the calling thread (never NULL). */

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libneox_zero1.so")
 NEOX_OK, NEOX_EINVAL, NEOX_EHIP, NEOX_ENOMEM = 0, -1, -2, -3
 NEOX_F16, NEOX_BF16 = 1, 2
 NEOX_SCALER_DYNAMIC, NEOX_SCALER_STATIC = 0, 1
+NEOX_OPT_ADAMW, NEOX_OPT_SGD = 0, 1
 NEOX_SEG_DECAY = 1
 NEOX_PAD_TENSOR = 0xFFFFFFFF
 
@@ -38,7 +39,8 @@ class neox_zero1_config(C.Structure):
                 ("min_scale", C.c_double), ("init_step", C.c_int64),
                 ("init_skipped", C.c_int64), ("init_good_steps", C.c_int32),
                 ("init_consecutive_overflows", C.c_int32), ("chunk_elems", C.c_uint32),
-                ("norm_blocks", C.c_uint32)]
+                ("norm_blocks", C.c_uint32), ("optimizer", C.c_int32),
+                ("segment_norms", C.c_uint32)]
 
 
 class neox_segment(C.Structure):
@@ -63,6 +65,8 @@ class neox_shard_segment(C.Structure):
 # Every symbol include/neox_zero1.h declares.
 EXPORTS = ("neox_zero1_default_config", "neox_zero1_partition", "neox_zero1_create",
            "neox_zero1_step", "neox_scaler_state", "neox_zero1_destroy",
+           "neox_zero1_step_local", "neox_zero1_step_apply", "neox_scaler_set",
+           "neox_zero1_segment_sumsq",
            "neox_zero1_timing_begin", "neox_zero1_timing_end", "neox_zero1_last_error")
 
 _lib = None
@@ -86,7 +90,11 @@ def lib():
         L.neox_zero1_step.argtypes = [C.c_void_p, C.c_float, C.c_void_p]
         L.neox_scaler_state.argtypes = [C.c_void_p, P(neox_scaler_state_t)]
         L.neox_zero1_destroy.argtypes = [C.c_void_p]
-        L.neox_zero1_timing_begin.argtypes = [C.c_void_p, C.c_int32]
+        L.neox_zero1_step_local.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+        L.neox_zero1_step_apply.argtypes = [C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]
+        L.neox_scaler_set.argtypes = [C.c_void_p, P(neox_scaler_state_t), C.c_void_p]
+        L.neox_zero1_segment_sumsq.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64]
+        L.neox_zero1_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
         L.neox_zero1_timing_end.argtypes = [C.c_void_p, P(C.c_double), P(C.c_int64)]
         L.neox_zero1_last_error.argtypes = []
         L.neox_zero1_last_error.restype = C.c_char_p
@@ -158,8 +166,37 @@ def neox_zero1_destroy(h: int):
     _check(lib().neox_zero1_destroy(C.c_void_p(h)))
 
 
-def neox_zero1_timing_begin(h: int, max_steps: int):
-    _check(lib().neox_zero1_timing_begin(C.c_void_p(h), max_steps))
+def neox_zero1_step_local(h: int, local_sumsq_ptr: int, stream_ptr: int = 0):
+    """Norm pass; this rank's squared norm goes to the device double at local_sumsq_ptr."""
+    _check(lib().neox_zero1_step_local(C.c_void_p(h), C.c_void_p(local_sumsq_ptr),
+                                       C.c_void_p(stream_ptr)))
+
+
+def neox_zero1_step_apply(h: int, global_sumsq_ptr: int, lr: float, stream_ptr: int = 0):
+    """Finalize on the device double at global_sumsq_ptr, then the update."""
+    _check(lib().neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(global_sumsq_ptr), C.c_float(lr),
+                                       C.c_void_p(stream_ptr)))
+
+
+def neox_scaler_set(h: int, loss_scale: float, good_steps=0, step=0, skipped_total=0,
+                    consecutive_overflows=0, stream_ptr: int = 0):
+    st = neox_scaler_state_t()
+    st.loss_scale = loss_scale
+    st.good_steps = good_steps
+    st.step = step
+    st.skipped_total = skipped_total
+    st.consecutive_overflows = consecutive_overflows
+    _check(lib().neox_scaler_set(C.c_void_p(h), C.byref(st), C.c_void_p(stream_ptr)))
+
+
+def neox_zero1_segment_sumsq(h: int, nseg: int):
+    out = (C.c_double * max(1, nseg))()
+    _check(lib().neox_zero1_segment_sumsq(C.c_void_p(h), out, nseg))
+    return list(out[:nseg])
+
+
+def neox_zero1_timing_begin(h: int, max_steps: int, update_only: bool = False):
+    _check(lib().neox_zero1_timing_begin(C.c_void_p(h), max_steps, int(update_only)))
 
 
 def neox_zero1_timing_end(h: int):
@@ -175,11 +212,14 @@ def neox_zero1_timing_end(h: int):
 # --------------------------------------------------------------------------------------
 
 def segment(grad, half, master, exp_avg, exp_avg_sq, decay: bool, tensor_id=0, tensor_offset=0):
-    """neox_segment over five 1-D CUDA tensors of equal length (no copies)."""
+    """neox_segment over five 1-D CUDA tensors of equal length (no copies); exp_avg_sq
+    may be None for the SGD optimizer."""
     import torch
     n = grad.numel()
     for t, dt in ((grad, None), (half, None), (master, torch.float32), (exp_avg, torch.float32),
                   (exp_avg_sq, torch.float32)):
+        if t is None:
+            continue
         if not t.is_cuda or t.numel() != n or not t.is_contiguous():
             raise ValueError("segment arrays must be contiguous CUDA tensors of equal length")
         if dt is not None and t.dtype != dt:
@@ -187,8 +227,8 @@ def segment(grad, half, master, exp_avg, exp_avg_sq, decay: bool, tensor_id=0, t
     if grad.dtype not in (torch.float16, torch.bfloat16) or half.dtype != grad.dtype:
         raise ValueError("grad and half must share float16 or bfloat16")
     return neox_segment(grad.data_ptr(), half.data_ptr(), master.data_ptr(), exp_avg.data_ptr(),
-                        exp_avg_sq.data_ptr(), n, NEOX_SEG_DECAY if decay else 0, tensor_id,
-                        tensor_offset)
+                        None if exp_avg_sq is None else exp_avg_sq.data_ptr(), n,
+                        NEOX_SEG_DECAY if decay else 0, tensor_id, tensor_offset)
 
 
 def current_stream_ptr() -> int:

@@ -59,6 +59,9 @@ struct neox_zero1 {
     uint32_t norm_blocks = 0;
     Chunk* d_chunks = nullptr;
     Chunk* d_norm_chunks = nullptr;
+    uint32_t nseg = 0;
+    uint32_t* d_seg_range = nullptr;   // per segment: [first, end) norm chunk (telemetry)
+    double* d_seg_sumsq = nullptr;     // per segment squared norm of the last step
     double* d_partial = nullptr;
     DevState* d_state = nullptr;
     hipStream_t last_stream = nullptr;
@@ -67,6 +70,7 @@ struct neox_zero1 {
     // profiling
     std::vector<TimingSlot> timing;
     int64_t timing_used = 0;
+    bool timing_update_only = false;
 };
 
 // ------------------------------------------------------------------------------------
@@ -123,6 +127,11 @@ static int validate_config(const neox_zero1_config* c) {
         (c->chunk_elems % kVec != 0 || c->chunk_elems < 256 || c->chunk_elems > (1u << 24)))
         return fail(NEOX_EINVAL, "chunk_elems %u: multiple of 8 in [256, 2^24]", c->chunk_elems);
     if (c->norm_blocks > (1u << 20)) return fail(NEOX_EINVAL, "norm_blocks %u too large", c->norm_blocks);
+    if (c->optimizer != NEOX_OPT_ADAMW && c->optimizer != NEOX_OPT_SGD)
+        return fail(NEOX_EINVAL, "optimizer %d", c->optimizer);
+    if (c->segment_norms > 1) return fail(NEOX_EINVAL, "segment_norms %u", c->segment_norms);
+    if (c->segment_norms && c->norm_blocks)
+        return fail(NEOX_EINVAL, "segment_norms needs the one-block-per-chunk norm pass (norm_blocks 0)");
     return NEOX_OK;
 }
 
@@ -189,7 +198,7 @@ static int vector_head(const neox_segment& s) {
     for (int h = 0; h < kVec; ++h) {
         if (aligned16((uintptr_t)s.grad + 2u * h) && aligned16((uintptr_t)s.half + 2u * h) &&
             aligned16((uintptr_t)s.master + 4u * h) && aligned16((uintptr_t)s.exp_avg + 4u * h) &&
-            aligned16((uintptr_t)s.exp_avg_sq + 4u * h))
+            (!s.exp_avg_sq || aligned16((uintptr_t)s.exp_avg_sq + 4u * h)))
             return h;
     }
     return -1;
@@ -202,7 +211,7 @@ static void push_chunk(std::vector<Chunk>& t, const neox_segment& s, uint32_t se
     c.half = static_cast<uint16_t*>(s.half) + start;
     c.master = s.master + start;
     c.m = s.exp_avg + start;
-    c.v = s.exp_avg_sq + start;
+    c.v = s.exp_avg_sq ? s.exp_avg_sq + start : nullptr;
     c.len = len;
     c.flags = ((s.flags & NEOX_SEG_DECAY) ? CH_DECAY : 0u) | (vec ? CH_VEC : 0u);
     c.seg = seg;
@@ -231,7 +240,7 @@ static bool overlaps(uintptr_t a, uint64_t abytes, uintptr_t b, uint64_t bbytes)
     return a < b + bbytes && b < a + abytes;
 }
 
-static int validate_segments(const neox_segment* segs, uint64_t nseg) {
+static int validate_segments(const neox_segment* segs, uint64_t nseg, bool need_v) {
     if (!segs) return fail(NEOX_EINVAL, "segs is NULL");
     if (nseg == 0) return fail(NEOX_EINVAL, "nseg is 0");
     if (nseg > (1u << 31)) return fail(NEOX_EINVAL, "too many segments");
@@ -240,7 +249,7 @@ static int validate_segments(const neox_segment* segs, uint64_t nseg) {
     ranges.reserve(nseg * 5);
     for (uint64_t i = 0; i < nseg; ++i) {
         const neox_segment& s = segs[i];
-        if (!s.grad || !s.half || !s.master || !s.exp_avg || !s.exp_avg_sq)
+        if (!s.grad || !s.half || !s.master || !s.exp_avg || (need_v && !s.exp_avg_sq))
             return fail(NEOX_EINVAL, "segment %llu: null array", (unsigned long long)i);
         if (s.numel == 0) return fail(NEOX_EINVAL, "segment %llu: numel is 0", (unsigned long long)i);
         if (s.numel > (UINT64_MAX >> 3)) return fail(NEOX_EINVAL, "segment %llu: numel too large", (unsigned long long)i);
@@ -252,7 +261,7 @@ static int validate_segments(const neox_segment* segs, uint64_t nseg) {
         ranges.push_back({(uintptr_t)s.half, 2 * s.numel, i});
         ranges.push_back({(uintptr_t)s.master, 4 * s.numel, i});
         ranges.push_back({(uintptr_t)s.exp_avg, 4 * s.numel, i});
-        ranges.push_back({(uintptr_t)s.exp_avg_sq, 4 * s.numel, i});
+        if (need_v) ranges.push_back({(uintptr_t)s.exp_avg_sq, 4 * s.numel, i});
     }
     // written arrays must not overlap each other (sorted sweep)
     std::sort(ranges.begin(), ranges.end(), [](const Range& a, const Range& b) { return a.p < b.p; });
@@ -273,6 +282,8 @@ static void free_handle(neox_zero1* h) {
             if (e) (void)hipEventDestroy(e);
     if (h->d_chunks) (void)hipFree(h->d_chunks);
     if (h->d_norm_chunks) (void)hipFree(h->d_norm_chunks);
+    if (h->d_seg_range) (void)hipFree(h->d_seg_range);
+    if (h->d_seg_sumsq) (void)hipFree(h->d_seg_sumsq);
     if (h->d_partial) (void)hipFree(h->d_partial);
     if (h->d_state) (void)hipFree(h->d_state);
     delete h;
@@ -285,7 +296,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     if (!cfg) return fail(NEOX_EINVAL, "cfg is NULL");
     int rc = validate_config(cfg);
     if (rc) return rc;
-    rc = validate_segments(segs, nseg);
+    rc = validate_segments(segs, nseg, cfg->optimizer == NEOX_OPT_ADAMW);
     if (rc) return rc;
 
     // update chunks of C elements; norm chunks of the smallest multiple of C that is
@@ -317,8 +328,22 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     if (nb == 0) nb = 1;
     h->norm_blocks = nb;
 
+    h->nseg = (uint32_t)nseg;
+    std::vector<uint32_t> seg_range;
+    if (cfg->segment_norms) {
+        // norm chunks are built segment by segment, so each segment owns a contiguous range
+        seg_range.assign(2 * nseg, 0);
+        for (uint32_t c = 0; c < h->nnorm; ++c) {
+            const uint32_t sg = norm_table[c].seg;
+            if (c == 0 || norm_table[c - 1].seg != sg) seg_range[2 * sg] = c;
+            seg_range[2 * sg + 1] = c + 1;
+        }
+    }
+
     e = hipMalloc(&h->d_chunks, table.size() * sizeof(Chunk));
     if (e == hipSuccess) e = hipMalloc(&h->d_norm_chunks, norm_table.size() * sizeof(Chunk));
+    if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_range, seg_range.size() * sizeof(uint32_t));
+    if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_sumsq, nseg * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_partial, nb * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_state, sizeof(DevState));
     if (e != hipSuccess) {
@@ -343,6 +368,9 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     e = hipMemcpyAsync(h->d_chunks, table.data(), table.size() * sizeof(Chunk), hipMemcpyHostToDevice, stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(h->d_norm_chunks, norm_table.data(), norm_table.size() * sizeof(Chunk),
+                           hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess && cfg->segment_norms)
+        e = hipMemcpyAsync(h->d_seg_range, seg_range.data(), seg_range.size() * sizeof(uint32_t),
                            hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(h->d_state, &st, sizeof st, hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -374,27 +402,89 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     return NEOX_OK;
 }
 
+// norm pass (+ per-segment sums when enabled)
+static hipError_t enqueue_norm(neox_zero1* h, hipStream_t stream) {
+    hipError_t e = launch_norm(h->cfg.dtype, h->d_norm_chunks, h->nnorm, h->norm_blocks,
+                               h->d_state, h->d_partial, stream);
+    if (e == hipSuccess && h->cfg.segment_norms)
+        e = launch_segment_sumsq(h->d_partial, h->d_seg_range, h->nseg, h->d_seg_sumsq, stream);
+    return e;
+}
+
+static hipError_t enqueue_update(neox_zero1* h, float lr, hipStream_t stream) {
+    UpdateArgs u = h->upd_base;
+    u.lr = lr;
+    return launch_update(h->cfg.dtype, h->cfg.optimizer, h->d_chunks, h->nchunks, h->d_state, u,
+                         stream);
+}
+
 extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
     if (!h) return fail(NEOX_EINVAL, "handle is NULL");
     if (!std::isfinite(lr)) return fail(NEOX_EINVAL, "lr %g is not finite", (double)lr);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    UpdateArgs u = h->upd_base;
-    u.lr = lr;
     TimingSlot* ts = nullptr;
     if (h->timing_used < (int64_t)h->timing.size()) ts = &h->timing[h->timing_used++];
 
+    const bool all = ts && !h->timing_update_only;
     hipError_t e = hipSuccess;
-    if (ts) e = hipEventRecord(ts->ev[0], stream);
-    if (e == hipSuccess)
-        e = launch_norm(h->cfg.dtype, h->d_norm_chunks, h->nnorm, h->norm_blocks, h->d_state,
-                        h->d_partial, stream);
-    if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[1], stream);
-    if (e == hipSuccess) e = launch_finalize(h->d_partial, h->norm_blocks, h->d_state, h->fin, stream);
+    if (all) e = hipEventRecord(ts->ev[0], stream);
+    if (e == hipSuccess) e = enqueue_norm(h, stream);
+    if (e == hipSuccess && all) e = hipEventRecord(ts->ev[1], stream);
+    if (e == hipSuccess) e = launch_finalize(h->d_partial, h->norm_blocks, nullptr, h->d_state, h->fin, stream);
     if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[2], stream);
-    if (e == hipSuccess) e = launch_update(h->cfg.dtype, h->d_chunks, h->nchunks, h->d_state, u, stream);
+    if (e == hipSuccess) e = enqueue_update(h, lr, stream);
     if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[3], stream);
     h->last_stream = stream;
     if (e != hipSuccess) return hip_fail(e, "step launch");
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_step_local(neox_zero1* h, double* local_sumsq, void* hip_stream) {
+    if (!h || !local_sumsq) return fail(NEOX_EINVAL, "null argument");
+    if ((uintptr_t)local_sumsq & 7u) return fail(NEOX_EINVAL, "local_sumsq not 8-byte aligned");
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = enqueue_norm(h, stream);
+    if (e == hipSuccess) e = launch_reduce(h->d_partial, h->norm_blocks, local_sumsq, stream);
+    h->last_stream = stream;
+    if (e != hipSuccess) return hip_fail(e, "step_local launch");
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_step_apply(neox_zero1* h, const double* global_sumsq, float lr,
+                                     void* hip_stream) {
+    if (!h || !global_sumsq) return fail(NEOX_EINVAL, "null argument");
+    if ((uintptr_t)global_sumsq & 7u) return fail(NEOX_EINVAL, "global_sumsq not 8-byte aligned");
+    if (!std::isfinite(lr)) return fail(NEOX_EINVAL, "lr %g is not finite", (double)lr);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = launch_finalize(nullptr, 0, global_sumsq, h->d_state, h->fin, stream);
+    if (e == hipSuccess) e = enqueue_update(h, lr, stream);
+    h->last_stream = stream;
+    if (e != hipSuccess) return hip_fail(e, "step_apply launch");
+    return NEOX_OK;
+}
+
+extern "C" int neox_scaler_set(neox_zero1* h, const neox_scaler_state_t* st, void* hip_stream) {
+    if (!h || !st) return fail(NEOX_EINVAL, "null argument");
+    if (!(std::isfinite(st->loss_scale) && st->loss_scale > 0.0f))
+        return fail(NEOX_EINVAL, "loss_scale %g", (double)st->loss_scale);
+    if (st->good_steps < 0 || st->step < 0 || st->skipped_total < 0 || st->consecutive_overflows < 0)
+        return fail(NEOX_EINVAL, "negative counter");
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = launch_set_state(h->d_state, st->loss_scale, st->good_steps, st->step,
+                                    st->skipped_total, st->consecutive_overflows,
+                                    h->fin.predivide_factor, h->fin.dp_world_size, stream);
+    h->last_stream = stream;
+    if (e != hipSuccess) return hip_fail(e, "scaler_set launch");
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg) {
+    if (!h || !out) return fail(NEOX_EINVAL, "null argument");
+    if (!h->cfg.segment_norms) return fail(NEOX_EINVAL, "handle created without segment_norms");
+    if (nseg != h->nseg) return fail(NEOX_EINVAL, "nseg %llu != %u", (unsigned long long)nseg, h->nseg);
+    hipError_t e = hipStreamSynchronize(h->last_stream);
+    if (e == hipSuccess) e = hipMemcpy(out, h->d_seg_sumsq, nseg * sizeof(double), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "segment_sumsq readback");
     return NEOX_OK;
 }
 
@@ -426,8 +516,10 @@ extern "C" int neox_zero1_destroy(neox_zero1* h) {
     return NEOX_OK;
 }
 
-extern "C" int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps) {
-    if (!h || max_steps < 1 || max_steps > 1000000) return fail(NEOX_EINVAL, "bad timing request");
+extern "C" int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only) {
+    if (!h || max_steps < 1 || max_steps > 1000000 || update_only < 0 || update_only > 1)
+        return fail(NEOX_EINVAL, "bad timing request");
+    h->timing_update_only = update_only != 0;
     for (auto& s : h->timing)
         for (auto& e : s.ev) (void)hipEventDestroy(e);
     h->timing.clear();
@@ -454,7 +546,7 @@ extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* st
         auto& s = h->timing[i];
         hipError_t r = hipEventSynchronize(s.ev[3]);
         if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
-        for (int k = 0; k < 3; ++k) {
+        for (int k = h->timing_update_only ? 2 : 0; k < 3; ++k) {
             float ms = 0.0f;
             r = hipEventElapsedTime(&ms, s.ev[k], s.ev[k + 1]);
             if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");

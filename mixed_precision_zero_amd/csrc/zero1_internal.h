@@ -71,10 +71,16 @@ struct UpdateArgs {
 // Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
                        const DevState* st, double* partial, hipStream_t stream);
-hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
-                           const FinalizeArgs& a, hipStream_t stream);
-hipError_t launch_update(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
-                         const UpdateArgs& a, hipStream_t stream);
+hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
+                           DevState* st, const FinalizeArgs& a, hipStream_t stream);
+hipError_t launch_reduce(const double* partial, uint32_t nparts, double* out, hipStream_t stream);
+hipError_t launch_segment_sumsq(const double* partial, const uint32_t* range, uint32_t nseg,
+                                double* out, hipStream_t stream);
+hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64_t step,
+                            int64_t skipped, int32_t consecutive, double predivide, double dp,
+                            hipStream_t stream);
+hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
+                         const DevState* st, const UpdateArgs& a, hipStream_t stream);
 
 // The unscale factor for scale s, computed in double and rounded once to FP32; the
 // host (initial state) and the finalize kernel evaluate the same expression.

@@ -198,12 +198,10 @@ __device__ __forceinline__ bool f32_finite(float x) {
 
 constexpr int kFinalizeBlock = 1024;
 
-__global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* __restrict__ partial,
-                                                                  uint32_t nparts,
-                                                                  DevState* __restrict__ st,
-                                                                  FinalizeArgs a) {
-    // fixed order: thread t owns partials t, t + 1024, ...; four independent loads per
-    // round keep the (one-block) read of up to a few MB of partials latency-tolerant
+// Fixed-order sum of the norm pass's partials by one block of kFinalizeBlock threads:
+// thread t owns partials t, t + 1024, ...; four independent loads per round keep the
+// one-block read of up to a few MB of partials latency-tolerant.
+__device__ __forceinline__ double sum_partials(const double* __restrict__ partial, uint32_t nparts) {
     double acc = 0.0;
     uint32_t i = threadIdx.x;
     for (; i + 3 * kFinalizeBlock < nparts; i += 4 * kFinalizeBlock) {
@@ -215,7 +213,49 @@ __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* 
         acc += p3;
     }
     for (; i < nparts; i += kFinalizeBlock) acc += partial[i];
-    const double sumsq = block_sum<kFinalizeBlock>(acc);
+    return block_sum<kFinalizeBlock>(acc);
+}
+
+// This rank's squared norm, for a caller that sums it over the data-parallel ranks.
+__global__ __launch_bounds__(kFinalizeBlock) void reduce_kernel(const double* __restrict__ partial,
+                                                                uint32_t nparts,
+                                                                double* __restrict__ out) {
+    const double s = sum_partials(partial, nparts);
+    if (threadIdx.x == 0) *out = s;
+}
+
+// Squared norm of each segment: the norm chunks of segment k are the contiguous range
+// [range[2k], range[2k+1]) of the norm table, one partial each.
+__global__ __launch_bounds__(kBlock) void segment_sumsq_kernel(const double* __restrict__ partial,
+                                                               const uint32_t* __restrict__ range,
+                                                               double* __restrict__ out) {
+    const uint32_t lo = range[2 * blockIdx.x], hi = range[2 * blockIdx.x + 1];
+    double acc = 0.0;
+    for (uint32_t i = lo + threadIdx.x; i < hi; i += kBlock) acc += partial[i];
+    const double s = block_sum<kBlock>(acc);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+// Stream-ordered overwrite of the persistent scaler state.
+__global__ void set_state_kernel(DevState* __restrict__ st, float scale, int32_t good_steps,
+                                 int64_t step, int64_t skipped, int32_t consecutive,
+                                 double predivide, double dp) {
+    if (threadIdx.x != 0) return;
+    st->loss_scale = scale;
+    st->good_steps = good_steps;
+    st->step = step;
+    st->skipped_total = skipped;
+    st->consecutive_overflows = consecutive;
+    st->inv = unscale_factor(predivide, dp, scale);
+}
+
+__global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* __restrict__ partial,
+                                                                  uint32_t nparts,
+                                                                  const double* __restrict__ sumsq_in,
+                                                                  DevState* __restrict__ st,
+                                                                  FinalizeArgs a) {
+    // the squared norm: this handle's own partials, or a value summed over the ranks
+    const double sumsq = sumsq_in ? *sumsq_in : sum_partials(partial, nparts);
     if (threadIdx.x != 0) return;
 
     float scale = st->loss_scale;
@@ -270,6 +310,16 @@ struct Coefs {
     float gs, rbc1, rsbc2;
 };
 
+// heavy-ball momentum SGD with decoupled decay: m = beta1*m + g; w -= lr*(m + wd*w)
+__device__ __forceinline__ void sgd(float h, float& w, float& m, const Coefs& c,
+                                    const UpdateArgs& a, bool decay) {
+    const float g = h * c.gs;
+    m = __builtin_fmaf(a.b1, m, g);
+    float u = m;
+    if (decay) u = __builtin_fmaf(a.wd, w, u);
+    w = __builtin_fmaf(-a.lr, u, w);
+}
+
 __device__ __forceinline__ void adam(float h, float& w, float& m, float& v, const Coefs& c,
                                      const UpdateArgs& a, bool decay) {
     const float g = h * c.gs;
@@ -281,10 +331,11 @@ __device__ __forceinline__ void adam(float h, float& w, float& m, float& v, cons
     w = __builtin_fmaf(-a.lr, u, w);
 }
 
-template <int DT, int U>
+template <int DT, int U, int OPT>
 __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict__ chunks,
                                                         const DevState* __restrict__ st,
                                                         UpdateArgs a) {
+    constexpr bool ADAM = OPT == 0;
     if (st->skip) return;
     // NZ1_UPDATE_REVERSE walks the chunks last-to-first, so the first gradients the
     // update reads are the ones the norm pass read last
@@ -319,8 +370,10 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
                     W[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(w4 + 2 * i + 1);
                     M[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(m4 + 2 * i);
                     M[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(m4 + 2 * i + 1);
-                    V[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i);
-                    V[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i + 1);
+                    if constexpr (ADAM) {
+                        V[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i);
+                        V[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i + 1);
+                    }
                 }
             }
 #pragma unroll
@@ -332,21 +385,31 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
                                   W[u][1].x, W[u][1].y, W[u][1].z, W[u][1].w};
                     float m[8] = {M[u][0].x, M[u][0].y, M[u][0].z, M[u][0].w,
                                   M[u][1].x, M[u][1].y, M[u][1].z, M[u][1].w};
-                    float v[8] = {V[u][0].x, V[u][0].y, V[u][0].z, V[u][0].w,
-                                  V[u][1].x, V[u][1].y, V[u][1].z, V[u][1].w};
+                    float v[8];
+                    if constexpr (ADAM) {
+                        v[0] = V[u][0].x; v[1] = V[u][0].y; v[2] = V[u][0].z; v[3] = V[u][0].w;
+                        v[4] = V[u][1].x; v[5] = V[u][1].y; v[6] = V[u][1].z; v[7] = V[u][1].w;
+                    }
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        adam(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], v[2 * k], c, a, decay);
-                        adam(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], v[2 * k + 1], c, a,
-                             decay);
+                        if constexpr (ADAM) {
+                            adam(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], v[2 * k], c, a, decay);
+                            adam(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], v[2 * k + 1], c,
+                                 a, decay);
+                        } else {
+                            sgd(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], c, a, decay);
+                            sgd(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], c, a, decay);
+                        }
                     }
                     constexpr bool NTS = NZ1_UPDATE_NT_STORE;
                     st16<NTS>(w4 + 2 * i, make_float4(w[0], w[1], w[2], w[3]));
                     st16<NTS>(w4 + 2 * i + 1, make_float4(w[4], w[5], w[6], w[7]));
                     st16<NTS>(m4 + 2 * i, make_float4(m[0], m[1], m[2], m[3]));
                     st16<NTS>(m4 + 2 * i + 1, make_float4(m[4], m[5], m[6], m[7]));
-                    st16<NTS>(v4 + 2 * i, make_float4(v[0], v[1], v[2], v[3]));
-                    st16<NTS>(v4 + 2 * i + 1, make_float4(v[4], v[5], v[6], v[7]));
+                    if constexpr (ADAM) {
+                        st16<NTS>(v4 + 2 * i, make_float4(v[0], v[1], v[2], v[3]));
+                        st16<NTS>(v4 + 2 * i + 1, make_float4(v[4], v[5], v[6], v[7]));
+                    }
                     st16<NTS>(h4 + i, make_uint4(Fmt<DT>::pack(w[0], w[1]), Fmt<DT>::pack(w[2], w[3]),
                                                  Fmt<DT>::pack(w[4], w[5]), Fmt<DT>::pack(w[6], w[7])));
                 }
@@ -356,11 +419,16 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
     }
     // scalar path: chunks that are not 16-byte aligned, and the last < 8 elements
     for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
-        float w = wp[i], m = mp[i], v = vp[i];
-        adam(Fmt<DT>::one(gp[i]), w, m, v, c, a, decay);
+        float w = wp[i], m = mp[i];
+        if constexpr (ADAM) {
+            float v = vp[i];
+            adam(Fmt<DT>::one(gp[i]), w, m, v, c, a, decay);
+            vp[i] = v;
+        } else {
+            sgd(Fmt<DT>::one(gp[i]), w, m, c, a, decay);
+        }
         wp[i] = w;
         mp[i] = m;
-        vp[i] = v;
         hp[i] = Fmt<DT>::enc(w);
     }
 }
@@ -379,18 +447,46 @@ hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
-                           const FinalizeArgs& a, hipStream_t stream) {
-    finalize_kernel<<<1, kFinalizeBlock, 0, stream>>>(partial, nparts, st, a);
+hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
+                           DevState* st, const FinalizeArgs& a, hipStream_t stream) {
+    finalize_kernel<<<1, kFinalizeBlock, 0, stream>>>(partial, nparts, sumsq_in, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_update(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
-                         const UpdateArgs& a, hipStream_t stream) {
+hipError_t launch_reduce(const double* partial, uint32_t nparts, double* out, hipStream_t stream) {
+    reduce_kernel<<<1, kFinalizeBlock, 0, stream>>>(partial, nparts, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_sumsq(const double* partial, const uint32_t* range, uint32_t nseg,
+                                double* out, hipStream_t stream) {
+    segment_sumsq_kernel<<<nseg, kBlock, 0, stream>>>(partial, range, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64_t step,
+                            int64_t skipped, int32_t consecutive, double predivide, double dp,
+                            hipStream_t stream) {
+    set_state_kernel<<<1, 64, 0, stream>>>(st, scale, good_steps, step, skipped, consecutive,
+                                           predivide, dp);
+    return hipGetLastError();
+}
+
+template <int OPT>
+static void launch_update_opt(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
+                              const UpdateArgs& a, hipStream_t stream) {
     if (dtype == 1)
-        update_kernel<1, kUpdateUnroll><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+        update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
     else
-        update_kernel<2, kUpdateUnroll><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+        update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+}
+
+hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
+                         const DevState* st, const UpdateArgs& a, hipStream_t stream) {
+    if (optimizer == 1)
+        launch_update_opt<1>(dtype, chunks, nchunks, st, a, stream);
+    else
+        launch_update_opt<0>(dtype, chunks, nchunks, st, a, stream);
     return hipGetLastError();
 }
 

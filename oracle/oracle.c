@@ -218,6 +218,36 @@ void orc_update(const orc_config* cfg, const orc_decision* d, float lr,
     }
 }
 
+/* Heavy-ball momentum SGD (Polyak; the form m = beta*m + g of Sutskever et al. 2013)
+ * with the same decoupled decay as the AdamW path; the OPT card (section "方法适配")
+ * reports SGD being tried in place of Adam.  The unscale, clip and skip are shared with
+ * AdamW; no bias correction. */
+void orc_update_sgd(const orc_config* cfg, const orc_decision* d, float lr,
+                    const uint16_t* grad, uint16_t* half, float* master, float* exp_avg,
+                    int64_t n, int32_t decay, double* s_m, double* s_w) {
+    if (d->skip) return;
+    const double mu = cfg->beta1, wd = cfg->weight_decay, rate = (double)lr;
+    for (int64_t i = 0; i < n; ++i) {
+        double x = orc_half_to_double(cfg->dtype, grad[i]);
+        double g = (x * d->inv) * d->coef;
+        double m0 = exp_avg[i], w0 = master[i];
+        double m1 = mu * m0 + g;
+        double u = m1;
+        if (decay) u += wd * w0;
+        double w1 = w0 - rate * u;
+
+        float wf = (float)w1;
+        exp_avg[i] = (float)m1;
+        master[i] = wf;
+        half[i] = orc_float_to_half(cfg->dtype, wf);
+
+        double sm = dmax(fabs(m1), dmax(mu * fabs(m0), fabs(g)));
+        double su = sm + (decay ? wd * fabs(w0) : 0.0);
+        if (s_m) s_m[i] = sm;
+        if (s_w) s_w[i] = dmax(fabs(w1), dmax(fabs(w0), rate * su));
+    }
+}
+
 void orc_step(const orc_config* cfg, orc_scaler* st, float lr,
               const orc_segment* segs, int64_t nseg) {
     double inv;
@@ -229,10 +259,15 @@ void orc_step(const orc_config* cfg, orc_scaler* st, float lr,
         orc_scan(cfg->dtype, segs[s].grad, segs[s].numel, inv, inv32, &sumsq, &overflow);
     orc_decision d;
     orc_decide(cfg, st, overflow, sumsq, &d);
-    for (int64_t s = 0; s < nseg; ++s)
-        orc_update(cfg, &d, lr, segs[s].grad, segs[s].half, segs[s].master, segs[s].exp_avg,
-                   segs[s].exp_avg_sq, segs[s].numel, segs[s].flags & ORC_DECAY,
-                   NULL, NULL, NULL);
+    for (int64_t s = 0; s < nseg; ++s) {
+        if (cfg->optimizer == ORC_SGD)
+            orc_update_sgd(cfg, &d, lr, segs[s].grad, segs[s].half, segs[s].master,
+                           segs[s].exp_avg, segs[s].numel, segs[s].flags & ORC_DECAY, NULL, NULL);
+        else
+            orc_update(cfg, &d, lr, segs[s].grad, segs[s].half, segs[s].master, segs[s].exp_avg,
+                       segs[s].exp_avg_sq, segs[s].numel, segs[s].flags & ORC_DECAY,
+                       NULL, NULL, NULL);
+    }
 }
 
 /* ------------------------------------------------------------------------------ */

@@ -47,6 +47,7 @@ extern "C" {
 #endif
 
 enum { ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_ADAMW = 0, ORC_SGD = 1 };
 enum { ORC_DYNAMIC = 0, ORC_STATIC = 1 };
 enum { ORC_DECAY = 1 };
 
@@ -59,6 +60,8 @@ typedef struct {
     int32_t scaler_mode;       /* ORC_DYNAMIC / ORC_STATIC                              */
     int32_t growth_interval;   /* clean steps between growths (dynamic mode)            */
     double growth_factor, backoff_factor, min_scale;
+    int32_t optimizer;         /* ORC_ADAMW, or ORC_SGD (momentum beta1, decoupled decay) */
+    int32_t pad_;
 } orc_config;
 
 typedef struct {
@@ -126,6 +129,12 @@ void orc_update(const orc_config* cfg, const orc_decision* d, float lr,
                 const uint16_t* grad, uint16_t* half, float* master, float* exp_avg,
                 float* exp_avg_sq, int64_t n, int32_t decay,
                 double* s_m, double* s_v, double* s_w);
+/* SGD with heavy-ball momentum on one run of elements (the optimizer the OPT card
+ * reports trying instead of Adam): m = beta1*m + g, w -= lr*(m + wd*w) for decaying
+ * elements.  exp_avg holds the momentum.  s_m, s_w as for orc_update. */
+void orc_update_sgd(const orc_config* cfg, const orc_decision* d, float lr,
+                    const uint16_t* grad, uint16_t* half, float* master, float* exp_avg,
+                    int64_t n, int32_t decay, double* s_m, double* s_w);
 /* One whole step over the segment list. */
 void orc_step(const orc_config* cfg, orc_scaler* st, float lr,
               const orc_segment* segs, int64_t nseg);

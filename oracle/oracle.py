@@ -15,6 +15,7 @@ from . import build as _build
 F16, BF16 = 1, 2
 DYNAMIC, STATIC = 0, 1
 DECAY = 1
+ADAMW, SGD = 0, 1
 
 _lib = None
 
@@ -34,7 +35,8 @@ class _Config(C.Structure):
                 ("predivide_factor", C.c_double), ("dp_world_size", C.c_int32),
                 ("dtype", C.c_int32), ("scaler_mode", C.c_int32),
                 ("growth_interval", C.c_int32), ("growth_factor", C.c_double),
-                ("backoff_factor", C.c_double), ("min_scale", C.c_double)]
+                ("backoff_factor", C.c_double), ("min_scale", C.c_double),
+                ("optimizer", C.c_int32), ("pad_", C.c_int32)]
 
 
 class _Scaler(C.Structure):
@@ -77,6 +79,8 @@ def _declare(L):
     L.orc_decide.argtypes = [P(_Config), P(_Scaler), C.c_int32, C.c_double, P(_Decision)]
     L.orc_update.argtypes = [P(_Config), P(_Decision), C.c_float] + [C.c_void_p] * 5 + \
         [C.c_int64, C.c_int32] + [C.c_void_p] * 3
+    L.orc_update_sgd.argtypes = [P(_Config), P(_Decision), C.c_float] + [C.c_void_p] * 4 + \
+        [C.c_int64, C.c_int32] + [C.c_void_p] * 2
     L.orc_step.argtypes = [P(_Config), P(_Scaler), C.c_float, P(_Segment), C.c_int64]
     L.orc_partition.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
                                 C.c_int64, P(_ShardSegment), C.c_int64, P(C.c_uint64)]
@@ -98,9 +102,10 @@ class Config:
     growth_factor: float = 2.0
     backoff_factor: float = 0.5
     min_scale: float = 1.0
+    optimizer: int = ADAMW
 
     def c(self):
-        return _Config(**dataclasses.asdict(self))
+        return _Config(**dataclasses.asdict(self), pad_=0)
 
 
 @dataclasses.dataclass
@@ -199,6 +204,24 @@ def update(cfg: Config, d: Decision, lr, grad, half, master, m, v, decay, scales
     return (sm, sv, sw) if scales else None
 
 
+def update_sgd(cfg: Config, d: Decision, lr, grad, half, master, m, decay, scales=False):
+    """In-place momentum SGD on host arrays; returns (s_m, s_w) when scales=True."""
+    n = grad.size
+    _check(grad, np.uint16, n)
+    _check(half, np.uint16, n)
+    for a in (master, m):
+        _check(a, np.float32, n)
+    cd = _Decision(d.skip, d.inv, d.inv32, d.coef, d.bc1, d.bc2, d.t)
+    sm = sw = None
+    if scales:
+        sm, sw = (np.zeros(n, np.float64) for _ in range(2))
+    nul = C.c_void_p(0)
+    lib().orc_update_sgd(C.byref(cfg.c()), C.byref(cd), lr, _ptr(grad), _ptr(half), _ptr(master),
+                         _ptr(m), n, int(bool(decay)), _ptr(sm) if scales else nul,
+                         _ptr(sw) if scales else nul)
+    return (sm, sw) if scales else None
+
+
 def step(cfg: Config, st: Scaler, lr, segments):
     """One whole step; segments = list of dicts with keys grad, half, master, m, v, decay."""
     arr = (_Segment * max(1, len(segments)))()
@@ -206,11 +229,11 @@ def step(cfg: Config, st: Scaler, lr, segments):
         n = s["grad"].size
         _check(s["grad"], np.uint16, n)
         _check(s["half"], np.uint16, n)
-        for k in ("master", "m", "v"):
+        for k in ("master", "m") + (() if cfg.optimizer == SGD else ("v",)):
             _check(s[k], np.float32, n)
+        v = _ptr(s["v"]).value if s.get("v") is not None else None
         arr[i] = _Segment(_ptr(s["grad"]).value, _ptr(s["half"]).value, _ptr(s["master"]).value,
-                          _ptr(s["m"]).value, _ptr(s["v"]).value, n,
-                          DECAY if s.get("decay", False) else 0, 0)
+                          _ptr(s["m"]).value, v, n, DECAY if s.get("decay", False) else 0, 0)
     cs = st.c()
     lib().orc_step(C.byref(cfg.c()), C.byref(cs), lr, arr, len(segments))
     st.load(cs)

@@ -47,7 +47,7 @@ def lib_config(w: W.Workload, **over):
         dp_world_size=h.dp_world_size, dtype=h.dtype, scaler_mode=h.scaler_mode,
         growth_interval=h.growth_interval, init_scale=h.init_scale,
         growth_factor=h.growth_factor, backoff_factor=h.backoff_factor,
-        min_scale=h.min_scale)
+        min_scale=h.min_scale, optimizer=h.optimizer)
     for k, v in over.items():
         setattr(cfg, k, v)
     return cfg
@@ -59,7 +59,8 @@ def oracle_config(w: W.Workload):
                     clip_norm=h.clip_norm, predivide_factor=h.predivide_factor,
                     dp_world_size=h.dp_world_size, dtype=h.dtype, scaler_mode=h.scaler_mode,
                     growth_interval=h.growth_interval, growth_factor=h.growth_factor,
-                    backoff_factor=h.backoff_factor, min_scale=h.min_scale)
+                    backoff_factor=h.backoff_factor, min_scale=h.min_scale,
+                    optimizer=h.optimizer)
 
 
 def u16(t):
@@ -85,21 +86,27 @@ class DeviceShard:
         self.flat = w.flat if flat is None else flat
         dt = torch_dtype(w.hyper.dtype)
         kinds = (dt, dt, torch.float32, torch.float32, torch.float32)
+        self.sgd = w.hyper.optimizer == 1
+        names = ARRAYS[:4] if self.sgd else ARRAYS     # SGD keeps no second moment
         self.segs = []                    # per segment: dict name -> 1-D tensor view
         if self.flat:
             n = w.numel
-            self.buffers = {}
-            for name, k, mis in zip(ARRAYS, kinds, misalign):
+            self.buffers = {"v": None}
+            for name, k, mis in zip(names, kinds, misalign):
                 self.buffers[name] = torch.empty(n + mis, dtype=k, device=device)[mis:]
             off = 0
             for numel, _ in w.segments:
-                self.segs.append({a: self.buffers[a][off:off + numel] for a in ARRAYS})
+                seg = {a: self.buffers[a][off:off + numel] for a in names}
+                seg.setdefault("v", None)
+                self.segs.append(seg)
                 off += numel
         else:
             self.buffers = None
             for numel, _ in w.segments:
-                self.segs.append({a: torch.empty(numel + mis, dtype=k, device=device)[mis:]
-                                  for a, k, mis in zip(ARRAYS, kinds, misalign)})
+                seg = {a: torch.empty(numel + mis, dtype=k, device=device)[mis:]
+                       for a, k, mis in zip(names, kinds, misalign)}
+                seg.setdefault("v", None)
+                self.segs.append(seg)
 
     def init_(self, seed_extra=0):
         if self.flat:
@@ -132,7 +139,7 @@ class DeviceShard:
         s = self.segs[i]
         return dict(grad=u16(s["grad"][lo:hi]), half=u16(s["half"][lo:hi]),
                     master=f32(s["master"][lo:hi]), m=f32(s["m"][lo:hi]),
-                    v=f32(s["v"][lo:hi]))
+                    v=None if s["v"] is None else f32(s["v"][lo:hi]))
 
     def host_grad_pieces(self, piece=1 << 28):
         for s in self.segs:
@@ -258,13 +265,18 @@ class Checker:
             tag = f"{where} seg {i} [{lo}:{hi})"
             if d.skip:
                 for k in ("half", "master", "m", "v"):
-                    assert np.array_equal(post[k], p[k]), f"{k}{tag} changed on a skipped step"
+                    if p[k] is not None:
+                        assert np.array_equal(post[k], p[k]), f"{k}{tag} changed on a skipped step"
                 continue
-            o = {k: p[k].copy() for k in ARRAYS}
-            sm, sv, sw = O.update(self.ocfg, d, np.float32(lr), o["grad"], o["half"], o["master"],
-                                  o["m"], o["v"], sh.decay(i), scales=True)
+            o = {k: (None if p[k] is None else p[k].copy()) for k in ARRAYS}
+            if sh.sgd:
+                sm, sw = O.update_sgd(self.ocfg, d, np.float32(lr), o["grad"], o["half"],
+                                      o["master"], o["m"], sh.decay(i), scales=True)
+            else:
+                sm, sv, sw = O.update(self.ocfg, d, np.float32(lr), o["grad"], o["half"],
+                                      o["master"], o["m"], o["v"], sh.decay(i), scales=True)
+                assert_close("exp_avg_sq", post["v"], o["v"], sv, tag)
             assert_close("exp_avg", post["m"], o["m"], sm, tag)
-            assert_close("exp_avg_sq", post["v"], o["v"], sv, tag)
             assert_close("master", post["master"], o["master"], sw, tag)
             assert_half_close(post["half"], o["half"], tag)
         return gst, d

@@ -124,7 +124,7 @@ def _fake_seg(n=16, base=0x10000, flags=0):
     ("dp_world_size", 0), ("dtype", 3), ("scaler_mode", 2), ("growth_interval", 0),
     ("init_scale", 0.0), ("init_scale", 1e39), ("growth_factor", 0.5), ("backoff_factor", 0.0),
     ("backoff_factor", 1.5), ("min_scale", 0.0), ("init_step", -1), ("chunk_elems", 100),
-    ("chunk_elems", 257), ("chunk_elems", 1 << 25)])
+    ("chunk_elems", 257), ("chunk_elems", 1 << 25), ("optimizer", 2), ("segment_norms", 2)])
 def test_create_rejects_bad_config(field, value):
     cfg = Z.neox_zero1_default_config()
     setattr(cfg, field, value)
@@ -145,6 +145,25 @@ def test_create_rejects_bad_segments(seg):
     with pytest.raises(Z.NeoxError) as e:
         Z.neox_zero1_create(Z.neox_zero1_default_config(), [seg])
     assert e.value.code == Z.NEOX_EINVAL
+
+
+def test_create_rejects_segment_norms_with_striding_norm_grid():
+    cfg = Z.neox_zero1_default_config(segment_norms=1, norm_blocks=4)
+    with pytest.raises(Z.NeoxError) as e:
+        Z.neox_zero1_create(cfg, [_fake_seg()])
+    assert e.value.code == Z.NEOX_EINVAL
+
+
+def test_create_exp_avg_sq_required_for_adamw_only():
+    seg = Z.neox_segment(0x1000, 0x2000, 0x3000, 0x4000, 0, 16, 0, 0, 0)
+    with pytest.raises(Z.NeoxError) as e:
+        Z.neox_zero1_create(Z.neox_zero1_default_config(), [seg])
+    assert "null array" in str(e.value)
+    # with SGD the missing second moment passes validation (creation then needs a GPU)
+    try:
+        Z.neox_zero1_create(Z.neox_zero1_default_config(optimizer=Z.NEOX_OPT_SGD), [seg])
+    except Z.NeoxError as e2:
+        assert e2.code != Z.NEOX_EINVAL or "null array" not in str(e2)
 
 
 def test_create_rejects_empty_and_null():
@@ -168,4 +187,8 @@ def test_null_handle_calls():
     assert L.neox_scaler_state(None, C.byref(st)) == Z.NEOX_EINVAL
     assert L.neox_zero1_destroy(None) == Z.NEOX_OK
     assert "null" in Z.neox_zero1_last_error().lower()
-    assert L.neox_zero1_timing_begin(None, 4) == Z.NEOX_EINVAL
+    assert L.neox_zero1_timing_begin(None, 4, 0) == Z.NEOX_EINVAL
+    assert L.neox_zero1_step_local(None, None, None) == Z.NEOX_EINVAL
+    assert L.neox_zero1_step_apply(None, None, C.c_float(1e-3), None) == Z.NEOX_EINVAL
+    assert L.neox_scaler_set(None, None, None) == Z.NEOX_EINVAL
+    assert L.neox_zero1_segment_sumsq(None, None, 0) == Z.NEOX_EINVAL

@@ -1,0 +1,250 @@
+"""GPU parity of the rows after the core step: the split step for data-parallel ranks,
+the scaler set / reset, per-segment norm telemetry, and the momentum-SGD variant."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_zero_amd as Z
+import workloads as W
+from gpu_harness import (Checker, DeviceShard, assert_close, assert_half_close, lib_config, log,
+                         oracle_config)
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _custom(name, sizes, decays, dtype=W.F16, steps=4, **hy):
+    return W.Workload(name, 910, list(zip(sizes, decays)), W.Hyper(dtype=dtype, **hy), steps=steps)
+
+
+def _outputs(shard):
+    torch.cuda.synchronize()
+    return {k: torch.cat([s[k].reshape(-1) for s in shard.segs]).clone()
+            for k in ("half", "master", "m", "v") if shard.segs[0][k] is not None}
+
+
+# ----------------------------------------------------------------------------------
+# split step
+# ----------------------------------------------------------------------------------
+
+def test_split_step_equals_step_on_one_rank():
+    """step == step_local followed by step_apply on the local value, bit for bit."""
+    w = _custom("split1", [70_001, 4096, 33], [True, False, True], clip_norm=0.05)
+    w.injections = {2: [(10, "nan")]}
+    stream = torch.cuda.current_stream().cuda_stream
+    outs, states = [], []
+    for mode in ("step", "split"):
+        sh = DeviceShard(w)
+        sh.init_()
+        h = Z.neox_zero1_create(lib_config(w), sh.neox_segments(), stream)
+        loc = torch.zeros(1, dtype=torch.float64, device="cuda")
+        st_seq = []
+        for k in range(5):
+            sh.grads_(k, Z.neox_scaler_state(h).loss_scale)
+            if mode == "step":
+                Z.neox_zero1_step(h, 1e-3, stream)
+            else:
+                Z.neox_zero1_step_local(h, loc.data_ptr(), stream)
+                Z.neox_zero1_step_apply(h, loc.data_ptr(), 1e-3, stream)
+            st = Z.neox_scaler_state(h)
+            st_seq.append((st.loss_scale, st.step, st.skipped_total, st.last_grad_norm,
+                           st.last_sumsq, st.last_clip_coef))
+        Z.neox_zero1_destroy(h)
+        outs.append(_outputs(sh))
+        states.append(st_seq)
+    assert states[0] == states[1]
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+def test_split_step_four_ranks_match_the_global_oracle():
+    """Four ZeRO-1 ranks of one model on this GPU: each runs step_local, the four local
+    squared norms are summed in rank order on the host and handed to every rank's
+    step_apply.  Decisions equal the oracle's on the whole model every step, clipping
+    is active, an inf in one rank's shard skips every rank, and every rank's elements
+    match the oracle's global step."""
+    tensors = [(50_000, True), (1_000, False), (120_011, True), (7, False), (30_000, True),
+               (2_048, False), (64_000, True)]
+    D, A = 4, 64
+    numel = [n for n, _ in tensors]
+    decay = [d for _, d in tensors]
+    hy = W.Hyper(clip_norm=0.02)
+    full = W.Workload("split4", 911, tensors, hy, grad_sigma=1e-4)
+    total = full.numel
+    stream = torch.cuda.current_stream().cuda_stream
+
+    ranks = []
+    for r in range(D):
+        segs, P = Z.neox_zero1_partition(numel, decay, D, r, A)
+        wr = W.Workload(f"rank{r}", 911, [(s.numel, bool(s.flags)) for s in segs], hy)
+        sh = DeviceShard(wr)
+        sh.init_(seed_extra=r)
+        chk = Checker(sh)
+        ranks.append(dict(P=P, lo=r * P, shard=sh, chk=chk,
+                          loc=torch.zeros(1, dtype=torch.float64, device="cuda"),
+                          glob=torch.zeros(1, dtype=torch.float64, device="cuda")))
+    padded = ranks[0]["P"] * D
+    ocfg = oracle_config(full)
+    ost = O.Scaler(loss_scale=hy.init_scale)
+    gfull = torch.zeros(padded, dtype=torch.float16, device="cuda")
+    lr = np.float32(1e-3)
+    try:
+        for k in range(5):
+            W.device_grads_(full, gfull[:total], k, ost.loss_scale)
+            if k == 3:   # overflow inside rank 2's shard only
+                gfull.view(torch.int16)[ranks[2]["lo"] + 5] = 0x7C00
+            for rk in ranks:
+                rk["shard"].buffers["grad"].copy_(gfull[rk["lo"]:rk["lo"] + rk["P"]])
+            torch.cuda.synchronize()
+            # oracle on the whole model
+            g_host = gfull.view(torch.int16).cpu().numpy().view(np.uint16)
+            inv, inv32 = O.unscale_factor(ocfg, ost)
+            sumsq, of = O.scan(W.F16, g_host, inv, inv32)
+            pre = [rk["shard"].host_window(i, 0, s["grad"].numel())
+                   for rk in ranks for i, s in enumerate(rk["shard"].segs)]
+            d = O.decide(ocfg, ost, of, sumsq)
+            # the ranks: local norms, rank-order sum on the host, apply
+            for rk in ranks:
+                Z.neox_zero1_step_local(rk["chk"].handle, rk["loc"].data_ptr(), stream)
+            total_sumsq = 0.0
+            for rk in ranks:
+                total_sumsq += float(rk["loc"].item())
+            for rk in ranks:
+                rk["glob"].fill_(total_sumsq)
+                Z.neox_zero1_step_apply(rk["chk"].handle, rk["glob"].data_ptr(), float(lr), stream)
+            j = 0
+            for r, rk in enumerate(ranks):
+                st = Z.neox_scaler_state(rk["chk"].handle)
+                assert (st.loss_scale, st.step, st.skipped_total, st.last_skipped) == \
+                    (ost.loss_scale, ost.step, ost.skipped_total, ost.last_skipped), (k, r)
+                if not d.skip:
+                    assert abs(st.last_grad_norm - ost.last_norm) <= 1e-5 * ost.last_norm
+                    assert st.last_clip_coef < 1.0
+                for i, s in enumerate(rk["shard"].segs):
+                    p = pre[j]
+                    j += 1
+                    post = rk["shard"].host_window(i, 0, s["grad"].numel())
+                    if d.skip:
+                        for a in ("half", "master", "m", "v"):
+                            assert np.array_equal(post[a], p[a]), (k, r, i, a)
+                        continue
+                    o = {a: p[a].copy() for a in ("grad", "half", "master", "m", "v")}
+                    sm, sv, sw = O.update(ocfg, d, lr, o["grad"], o["half"], o["master"], o["m"],
+                                          o["v"], rk["shard"].decay(i), scales=True)
+                    tag = f" step {k} rank {r} seg {i}"
+                    assert_close("exp_avg", post["m"], o["m"], sm, tag)
+                    assert_close("exp_avg_sq", post["v"], o["v"], sv, tag)
+                    assert_close("master", post["master"], o["master"], sw, tag)
+                    assert_half_close(post["half"], o["half"], tag)
+            log(f"  step {k}: skip={d.skip} norm={ost.last_norm:.4g} ranks agree with the oracle")
+        assert ost.skipped_total == 1
+    finally:
+        for rk in ranks:
+            rk["chk"].close()
+
+
+# ----------------------------------------------------------------------------------
+# scaler set / reset
+# ----------------------------------------------------------------------------------
+
+def test_scaler_reset_after_collapse():
+    """Drive the scale to its floor with overflows, reset it to 2^16 with
+    neox_scaler_set (the OPT card's remedy), and keep matching the oracle."""
+    w = _custom("reset", [40_000, 999], [True, False], min_scale=1.0)
+    w.injections = {k: [(123 + k, "+inf")] for k in range(1, 19)}
+    sh = DeviceShard(w)
+    sh.init_()
+    chk = Checker(sh)
+    try:
+        for k in range(20):
+            if k == 19:
+                st = Z.neox_scaler_state(chk.handle)
+                assert st.loss_scale == 1.0 and st.consecutive_overflows == 18
+                Z.neox_scaler_set(chk.handle, 65536.0, good_steps=0, step=st.step,
+                                  skipped_total=st.skipped_total, consecutive_overflows=0,
+                                  stream_ptr=torch.cuda.current_stream().cuda_stream)
+                chk.ost.loss_scale, chk.ost.good_steps, chk.ost.consecutive_overflows = 65536.0, 0, 0
+                st = Z.neox_scaler_state(chk.handle)
+                assert (st.loss_scale, st.consecutive_overflows) == (65536.0, 0)
+            sh.grads_(k, chk.scale())
+            chk.step(6e-4, where=f" reset step {k}")
+        assert chk.ost.step == 2 and chk.ost.skipped_total == 18
+    finally:
+        chk.close()
+
+
+def test_scaler_set_rejects_bad_state():
+    w = _custom("reset_bad", [1024], [True])
+    sh = DeviceShard(w)
+    sh.init_()
+    h = Z.neox_zero1_create(lib_config(w), sh.neox_segments(), 0)
+    try:
+        for bad in (dict(loss_scale=0.0), dict(loss_scale=float("inf")),
+                    dict(loss_scale=1.0, step=-1)):
+            with pytest.raises(Z.NeoxError):
+                Z.neox_scaler_set(h, **bad)
+    finally:
+        Z.neox_zero1_destroy(h)
+
+
+# ----------------------------------------------------------------------------------
+# per-segment telemetry
+# ----------------------------------------------------------------------------------
+
+def test_segment_norms_match_oracle():
+    """Each segment's squared norm of the unscaled gradient matches the oracle's scan of
+    that segment; they add up to the step's squared norm; an overflow shows in the
+    segment that holds it."""
+    sizes = [100_000, 3, 65_536, 17, 4096 * 5 + 1, 250_000]
+    w = _custom("telemetry", sizes, [True, False, True, False, True, True])
+    w.injections = {1: [(100_000 + 3 + 500, "nan")]}     # inside segment 2
+    sh = DeviceShard(w)
+    sh.init_()
+    chk = Checker(sh, segment_norms=1)
+    try:
+        for k in range(3):
+            sh.grads_(k, chk.scale())
+            inv, inv32 = O.unscale_factor(chk.ocfg, chk.ost)
+            want = [O.scan(W.F16, sh.host_window(i, 0, n)["grad"], inv, inv32) for i, (n, _) in
+                    enumerate(w.segments)]
+            chk.step(6e-4, where=f" telemetry step {k}")
+            got = Z.neox_zero1_segment_sumsq(chk.handle, len(sizes))
+            st = Z.neox_scaler_state(chk.handle)
+            for i, ((ws, wof), g) in enumerate(zip(want, got)):
+                if wof:
+                    assert not np.isfinite(g), (k, i)
+                else:
+                    assert np.isfinite(g) and abs(g - ws) <= 1e-5 * ws, (k, i, g, ws)
+            if not st.last_skipped:
+                assert abs(sum(got) - st.last_sumsq) <= 1e-12 * st.last_sumsq
+            else:
+                assert k == 1 and [np.isfinite(g) for g in got] == [True, True, False, True, True, True]
+    finally:
+        chk.close()
+
+
+# ----------------------------------------------------------------------------------
+# momentum SGD
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("misalign", [(0, 0, 0, 0, 0), (1, 2, 3, 1, 0)], ids=["aligned", "mixed"])
+def test_sgd_parity(dtype, misalign):
+    """Momentum SGD (exp_avg = momentum, no second moment) on ragged segments, both
+    formats, aligned and unaligned arrays, with one skipped step."""
+    sizes = [1, 9, 255, 4097, 33_333, 8, 70_000]
+    extra = dict(scaler_mode=W.STATIC, init_scale=1.0) if dtype == W.BF16 else {}
+    w = _custom("sgd", sizes, [i % 2 == 0 for i in range(len(sizes))], dtype, optimizer=1,
+                weight_decay=0.05, clip_norm=0.5, **extra)
+    w.grad_sigma = 1e-3
+    w.injections = {2: [(4000, "-inf")]}
+    sh = DeviceShard(w, misalign=misalign)
+    sh.init_()
+    chk = Checker(sh, chunk_elems=1024)
+    try:
+        for k in range(5):
+            sh.grads_(k, chk.scale())
+            chk.step(1e-2, where=f" sgd step {k}")
+        assert chk.ost.skipped_total == 1
+    finally:
+        chk.close()

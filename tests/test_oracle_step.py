@@ -458,3 +458,75 @@ def test_resident_bytes_per_param():
                  + s["half"].itemsize + np.dtype(np.uint16).itemsize)
     assert per_param == vals["bytes_per_param"]
     assert abs(vals["params"] * per_param - vals["total_bytes_approx"]) / 2.8e12 < 0.01
+
+
+# ----------------------------------------------------------------------------------
+# SGD with heavy-ball momentum (the alternative optimizer the OPT card reports trying)
+# ----------------------------------------------------------------------------------
+
+def _sgd_step(cfg, st, lr, grad, s, decay):
+    return O.step(cfg, st, lr, [dict(grad=grad, decay=decay, half=s["half"], master=s["master"],
+                                     m=s["m"], v=None)])
+
+
+@pytest.mark.parametrize("decay", [True, False])
+def test_sgd_first_step_closed_form(decay):
+    """From zero momentum: m1 = g and w1 = w0 - lr*(g + wd*w0 [decay])."""
+    n = 2048
+    rng = np.random.default_rng(50)
+    S = 512.0
+    grad = grads_from(rng.standard_normal(n) * 1e-2 * S)
+    g = O.half_to_double(O.F16, grad) / S
+    cfg = O.Config(optimizer=O.SGD, beta1=0.9, weight_decay=0.1, clip_norm=0.0)
+    st = O.Scaler(loss_scale=S)
+    s = make_state(n, 51)
+    w0 = s["master"].astype(np.float64)
+    lr = np.float32(1e-2)
+    _sgd_step(cfg, st, lr, grad, s, decay)
+    assert ulps32(s["m"], g.astype(np.float32)).max() <= 0
+    want = w0 - float(lr) * (g + (cfg.weight_decay * w0 if decay else 0.0))
+    assert ulps32(s["master"], want.astype(np.float32)).max() <= 1
+
+
+def test_sgd_constant_gradient_geometric_momentum():
+    """Constant g, no decay: m_t = g (1 - mu^t)/(1 - mu) and
+    w_T = w0 - lr * g * sum_{t=1..T} (1 - mu^t)/(1 - mu)."""
+    n, T, mu = 512, 15, 0.8
+    rng = np.random.default_rng(52)
+    grad = grads_from(rng.standard_normal(n) * 1e-2)
+    g = O.half_to_double(O.F16, grad)
+    cfg = O.Config(optimizer=O.SGD, beta1=mu, weight_decay=0.0, clip_norm=0.0,
+                   growth_interval=10 ** 6)
+    st = O.Scaler(loss_scale=1.0)
+    s = make_state(n, 53)
+    w0 = s["master"].astype(np.float64)
+    wmax = np.abs(w0)
+    lr = np.float32(1e-3)
+    for t in range(1, T + 1):
+        _sgd_step(cfg, st, lr, grad, s, False)
+        mt = g * (1 - mu ** t) / (1 - mu)
+        assert (np.abs(s["m"] - mt) <= t * F32_EPS * np.abs(mt)).all(), t
+    want = w0 - float(lr) * g * sum((1 - mu ** t) / (1 - mu) for t in range(1, T + 1))
+    wmax = np.maximum(wmax, np.abs(want))
+    assert (np.abs(s["master"] - want) <= T * F32_EPS * wmax).all()
+
+
+def test_sgd_zero_momentum_is_plain_sgd_and_skip_is_untouched():
+    n = 300
+    rng = np.random.default_rng(54)
+    cfg = O.Config(optimizer=O.SGD, beta1=0.0, weight_decay=0.0, clip_norm=0.0)
+    st = O.Scaler(loss_scale=1.0)
+    s = make_state(n, 55)
+    lr = np.float32(1e-2)
+    for _ in range(3):
+        w0 = s["master"].astype(np.float64)
+        grad = grads_from(rng.standard_normal(n) * 0.1)
+        _sgd_step(cfg, st, lr, grad, s, False)
+        want = w0 - float(lr) * O.half_to_double(O.F16, grad)
+        assert ulps32(s["master"], want.astype(np.float32)).max() <= 1
+    grad[17] = 0x7C00
+    before = {k: v.copy() for k, v in s.items()}
+    _sgd_step(cfg, st, lr, grad, s, False)
+    for k in s:
+        assert np.array_equal(s[k], before[k])
+    assert st.last_skipped == 1 and st.step == 3

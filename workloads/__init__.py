@@ -46,6 +46,7 @@ class Hyper:
     growth_factor: float = 2.0
     backoff_factor: float = 0.5
     min_scale: float = 1.0
+    optimizer: int = 0             # 0 AdamW, 1 momentum SGD (no second moment)
 
 
 @dataclasses.dataclass
@@ -271,7 +272,8 @@ def device_init_(w: Workload, master, half, m, v, seed_extra: int = 0):
     device_normal_(master, w.master_sigma, _torch_seed(w.wid, 0, seed_extra))
     half.copy_(master)
     m.zero_()
-    v.zero_()
+    if v is not None:
+        v.zero_()
 
 
 def device_grads_(w: Workload, grad, step: int, scale: float, offset: int = 0,
