@@ -215,6 +215,8 @@ def main():
                     help="time the split step (step_local + step_apply on the local value)")
     ap.add_argument("--segment-norms", action="store_true",
                     help="keep per-segment squared norms (telemetry) during the step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--no-timing-events", action="store_true",
                     help="time whole steps only (no per-kernel events)")
     ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
@@ -307,13 +309,22 @@ def main():
 
     for _ in range(args.warmup):
         one_step()
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            Z.neox_zero1_step(h, w.hyper.lr, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        one_step = graph.replay
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
           flush=True)
 
     # The timed steps record only the update kernel's two events; the norm / finalize
     # split comes from a short pass with all events after the timed region.
-    timed_events = not args.no_timing_events and not args.split
+    timed_events = not args.no_timing_events and not args.split and not args.graph
     if timed_events:
         Z.neox_zero1_timing_begin(h, args.steps, update_only=True)
     torch.cuda.synchronize()
@@ -357,7 +368,7 @@ def main():
                    "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
                    "layout": "flat shard" if w.flat else "separate allocations",
                    "optimizer": args.optimizer, "split": args.split,
-                   "segment_norms": args.segment_norms},
+                   "segment_norms": args.segment_norms, "graph": args.graph},
         "hbm": {"step_bytes": step_bpp * n,
                 "step_gbps": step_bpp * n / (ms_per_step * 1e-3) / 1e9,
                 "step_frac_of_peak": step_bpp * n / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},

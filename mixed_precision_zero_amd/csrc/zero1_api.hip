@@ -42,6 +42,14 @@ int hip_fail(hipError_t e, const char* what) {
 #ifndef NZ1_NORM_CHUNK
 #define NZ1_NORM_CHUNK 16384
 #endif
+// Blocks per CU for each pass (0 = as many as registers allow).  The cap is enforced by
+// reserving an equal share of the CU's LDS per block.
+#ifndef NZ1_UPDATE_BLOCKS_PER_CU
+#define NZ1_UPDATE_BLOCKS_PER_CU 0
+#endif
+#ifndef NZ1_NORM_BLOCKS_PER_CU
+#define NZ1_NORM_BLOCKS_PER_CU 0
+#endif
 constexpr uint32_t kDefaultChunk = NZ1_UPDATE_CHUNK;
 constexpr uint32_t kNormChunk = NZ1_NORM_CHUNK;
 
@@ -57,6 +65,8 @@ struct neox_zero1 {
     uint32_t nchunks = 0;          // update work units
     uint32_t nnorm = 0;            // norm-pass work units
     uint32_t norm_blocks = 0;
+    uint32_t update_lds = 0;       // LDS reserved per update block (occupancy cap)
+    uint32_t norm_lds = 0;         // LDS reserved per norm block
     Chunk* d_chunks = nullptr;
     Chunk* d_norm_chunks = nullptr;
     uint32_t nseg = 0;
@@ -321,6 +331,15 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) { free_handle(h); return hip_fail(e, "hipGetDevice"); }
+    int lds_per_cu = 0;
+    e = hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              h->device);
+    if (e != hipSuccess) { free_handle(h); return hip_fail(e, "hipDeviceGetAttribute"); }
+    auto reserve = [&](uint32_t per_cu) -> uint32_t {
+        return per_cu ? (uint32_t)(lds_per_cu / per_cu) & ~1023u : 0u;
+    };
+    h->update_lds = reserve(NZ1_UPDATE_BLOCKS_PER_CU);
+    h->norm_lds = reserve(NZ1_NORM_BLOCKS_PER_CU);
     h->nnorm = (uint32_t)norm_table.size();
     // norm pass: one block per norm chunk unless a smaller striding grid is requested
     uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : h->nnorm;
@@ -405,7 +424,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 // norm pass (+ per-segment sums when enabled)
 static hipError_t enqueue_norm(neox_zero1* h, hipStream_t stream) {
     hipError_t e = launch_norm(h->cfg.dtype, h->d_norm_chunks, h->nnorm, h->norm_blocks,
-                               h->d_state, h->d_partial, stream);
+                               h->d_state, h->d_partial, h->norm_lds, stream);
     if (e == hipSuccess && h->cfg.segment_norms)
         e = launch_segment_sumsq(h->d_partial, h->d_seg_range, h->nseg, h->d_seg_sumsq, stream);
     return e;
@@ -415,7 +434,7 @@ static hipError_t enqueue_update(neox_zero1* h, float lr, hipStream_t stream) {
     UpdateArgs u = h->upd_base;
     u.lr = lr;
     return launch_update(h->cfg.dtype, h->cfg.optimizer, h->d_chunks, h->nchunks, h->d_state, u,
-                         stream);
+                         h->update_lds, stream);
 }
 
 extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace nz1 {
@@ -46,12 +47,14 @@ struct alignas(64) DevState {
     float last_clip_coef;
     // handed from the finalize to the passes
     float inv;                   // fp32(f / (D * S)) for the next norm pass
+    int32_t pad_[3];
+    // what the update reads, in one 16-byte block (one scalar load)
+    int32_t skip;                // this step's decision
     float gscale;                // this step's unscale factor times clip coefficient
     float rbc1;                  // 1 / (1 - beta1^t)
     float rsbc2;                 // 1 / sqrt(1 - beta2^t)
-    int32_t skip;                // this step's decision
-    int32_t pad_;
 };
+static_assert(offsetof(DevState, skip) % 16 == 0, "update fields share one 16-byte load");
 
 struct FinalizeArgs {
     double clip_norm;
@@ -70,7 +73,8 @@ struct UpdateArgs {
 
 // Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
-                       const DevState* st, double* partial, hipStream_t stream);
+                       const DevState* st, double* partial, uint32_t lds_reserve,
+                       hipStream_t stream);
 hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
                            DevState* st, const FinalizeArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const double* partial, uint32_t nparts, double* out, hipStream_t stream);
@@ -80,7 +84,8 @@ hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64
                             int64_t skipped, int32_t consecutive, double predivide, double dp,
                             hipStream_t stream);
 hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
-                         const DevState* st, const UpdateArgs& a, hipStream_t stream);
+                         const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
+                         hipStream_t stream);
 
 // The unscale factor for scale s, computed in double and rounded once to FP32; the
 // host (initial state) and the finalize kernel evaluate the same expression.

@@ -85,35 +85,47 @@ struct Fmt<2> {
 #ifndef NZ1_UPDATE_REVERSE
 #define NZ1_UPDATE_REVERSE 1
 #endif
+#ifndef NZ1_UPDATE_FAST_DIV
+#define NZ1_UPDATE_FAST_DIV 0
+#endif
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// The arrays are device (global) memory; the pointers come out of the work table, so
+// the compiler cannot prove it and would emit generic flat accesses.  Accessing them
+// through address-space-1 pointers gives global_load / global_store.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 
 template <bool NT>
 __device__ __forceinline__ uint4 ld16(const uint4* p) {
+    const g_u32x4* q = (const g_u32x4*)p;
     u32x4 r;
-    if constexpr (NT) r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    else r = *reinterpret_cast<const u32x4*>(p);
+    if constexpr (NT) r = __builtin_nontemporal_load(q);
+    else r = *q;
     return make_uint4(r.x, r.y, r.z, r.w);
 }
 template <bool NT>
 __device__ __forceinline__ float4 ld16(const float4* p) {
+    const g_f32x4* q = (const g_f32x4*)p;
     f32x4 r;
-    if constexpr (NT) r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    else r = *reinterpret_cast<const f32x4*>(p);
+    if constexpr (NT) r = __builtin_nontemporal_load(q);
+    else r = *q;
     return make_float4(r.x, r.y, r.z, r.w);
 }
 template <bool NT>
 __device__ __forceinline__ void st16(uint4* p, uint4 v) {
+    g_u32x4* q = (g_u32x4*)p;
     const u32x4 r = {v.x, v.y, v.z, v.w};
-    if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
-    else *reinterpret_cast<u32x4*>(p) = r;
+    if constexpr (NT) __builtin_nontemporal_store(r, q);
+    else *q = r;
 }
 template <bool NT>
 __device__ __forceinline__ void st16(float4* p, float4 v) {
+    g_f32x4* q = (g_f32x4*)p;
     const f32x4 r = {v.x, v.y, v.z, v.w};
-    if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
-    else *reinterpret_cast<f32x4*>(p) = r;
+    if constexpr (NT) __builtin_nontemporal_store(r, q);
+    else *q = r;
 }
 
 // ------------------------------------------------------------------------------------
@@ -320,35 +332,60 @@ __device__ __forceinline__ void sgd(float h, float& w, float& m, const Coefs& c,
     w = __builtin_fmaf(-a.lr, u, w);
 }
 
+// Square root and reciprocal with the hardware's ~1-ulp instructions.  v_sqrt_f32 is
+// given a normal input: a subnormal v is scaled by 2^64 first and the root by 2^-32
+// (exact powers of two).  The reciprocal's input sqrt(v)/sqrt(bc2) + eps is never
+// subnormal (sqrt of the smallest FP32 subnormal is ~3.7e-23), so v_rcp_f32 sees
+// normal numbers, zero or infinity.
+__device__ __forceinline__ float sqrt_hw(float v) {
+    const bool tiny = v < 0x1p-126f;
+    const float r = __builtin_amdgcn_sqrtf(tiny ? v * 0x1p64f : v);
+    return tiny ? r * 0x1p-32f : r;
+}
+
 __device__ __forceinline__ void adam(float h, float& w, float& m, float& v, const Coefs& c,
                                      const UpdateArgs& a, bool decay) {
     const float g = h * c.gs;
     m = __builtin_fmaf(a.b1, m, a.omb1 * g);
     v = __builtin_fmaf(a.b2, v, a.omb2 * (g * g));
+#if NZ1_UPDATE_FAST_DIV
+    const float den = __builtin_fmaf(sqrt_hw(v), c.rsbc2, a.eps);
+    float u = (m * c.rbc1) * __builtin_amdgcn_rcpf(den);
+#else
     const float den = __builtin_fmaf(__builtin_sqrtf(v), c.rsbc2, a.eps);
     float u = (m * c.rbc1) / den;
+#endif
     if (decay) u = __builtin_fmaf(a.wd, w, u);
     w = __builtin_fmaf(-a.lr, u, w);
 }
 
 template <int DT, int U, int OPT>
 __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict__ chunks,
+                                                        uint32_t nchunks,
                                                         const DevState* __restrict__ st,
                                                         UpdateArgs a) {
     constexpr bool ADAM = OPT == 0;
-    if (st->skip) return;
     // NZ1_UPDATE_REVERSE walks the chunks last-to-first, so the first gradients the
-    // update reads are the ones the norm pass read last
-    const Chunk* ch = chunks + (NZ1_UPDATE_REVERSE ? gridDim.x - 1 - blockIdx.x : blockIdx.x);
+    // update reads are the ones the norm pass read last.
+    const Chunk* ch = chunks + (NZ1_UPDATE_REVERSE ? nchunks - 1 - blockIdx.x : blockIdx.x);
+    // The descriptor and the finalize's decision are fetched together: the early exit
+    // below tests both, so neither load waits for the other.
     const uint32_t len = ch->len;
     const uint32_t flags = ch->flags;
-    const bool decay = (flags & CH_DECAY) != 0;
     const uint16_t* __restrict__ gp = ch->grad;
     uint16_t* __restrict__ hp = ch->half;
     float* __restrict__ wp = ch->master;
     float* __restrict__ mp = ch->m;
     float* __restrict__ vp = ch->v;
+    const int32_t skip = st->skip;
     const Coefs c{st->gscale, st->rbc1, st->rsbc2};
+    // Chunks are never empty, their pointers are at least 2-byte aligned and flags use
+    // the low bits only, so the last two terms never fire; they make the branch wait for
+    // the whole descriptor at once.
+    const uint32_t odd = (uint32_t)(((uintptr_t)gp | (uintptr_t)hp | (uintptr_t)wp |
+                                     (uintptr_t)mp | (uintptr_t)vp) & 1u) | (flags >> 31);
+    if (skip | (len == 0) | odd) return;
+    const bool decay = (flags & CH_DECAY) != 0;
 
     uint32_t done = 0;
     if (flags & CH_VEC) {
@@ -439,11 +476,12 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
 constexpr int kUpdateUnroll = NZ1_UPDATE_UNROLL;
 
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
-                       const DevState* st, double* partial, hipStream_t stream) {
+                       const DevState* st, double* partial, uint32_t lds_reserve,
+                       hipStream_t stream) {
     if (dtype == 1)
-        norm_kernel<1><<<blocks, kBlock, 0, stream>>>(chunks, nchunks, st, partial);
+        norm_kernel<1><<<blocks, kBlock, lds_reserve, stream>>>(chunks, nchunks, st, partial);
     else
-        norm_kernel<2><<<blocks, kBlock, 0, stream>>>(chunks, nchunks, st, partial);
+        norm_kernel<2><<<blocks, kBlock, lds_reserve, stream>>>(chunks, nchunks, st, partial);
     return hipGetLastError();
 }
 
@@ -474,19 +512,22 @@ hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64
 
 template <int OPT>
 static void launch_update_opt(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
-                              const UpdateArgs& a, hipStream_t stream) {
+                              const UpdateArgs& a, uint32_t lds, hipStream_t stream) {
     if (dtype == 1)
-        update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+        update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kBlock, lds, stream>>>(chunks, nchunks, st, a);
     else
-        update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kBlock, 0, stream>>>(chunks, st, a);
+        update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kBlock, lds, stream>>>(chunks, nchunks, st, a);
 }
 
+// lds_reserve: dynamic LDS the kernel never touches, requested only to cap how many
+// blocks share a CU (fewer tiles in flight keep the chip's open DRAM rows few).
 hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
-                         const DevState* st, const UpdateArgs& a, hipStream_t stream) {
+                         const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
+                         hipStream_t stream) {
     if (optimizer == 1)
-        launch_update_opt<1>(dtype, chunks, nchunks, st, a, stream);
+        launch_update_opt<1>(dtype, chunks, nchunks, st, a, lds_reserve, stream);
     else
-        launch_update_opt<0>(dtype, chunks, nchunks, st, a, stream);
+        launch_update_opt<0>(dtype, chunks, nchunks, st, a, lds_reserve, stream);
     return hipGetLastError();
 }
 
