@@ -78,7 +78,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+                              "`python -m mixed_precision_zero_amd.build`")
         L = C.CDLL(LIB_PATH)
         P = C.POINTER
         L.neox_zero1_default_config.argtypes = [P(neox_zero1_config)]

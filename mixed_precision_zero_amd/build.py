@@ -14,6 +14,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit contraction: every fused multiply-add in the kernels is written out
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
 ]

@@ -279,4 +279,9 @@ class Checker:
             assert_close("exp_avg", post["m"], o["m"], sm, tag)
             assert_close("master", post["master"], o["master"], sw, tag)
             assert_half_close(post["half"], o["half"], tag)
+            # the half copy is exactly the stored FP32 master rounded to the half format
+            own = O.float_to_half(self.w.hyper.dtype, post["master"])
+            bad = post["half"] != own
+            assert not bad.any(), (f"half{tag}: {int(bad.sum())} elements differ from the "
+                                   f"cast of the GPU's own master")
         return gst, d
