@@ -187,11 +187,13 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
 int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream);
 
-/* Wait for the last enqueued step (its stream) and copy the state to *out.
- * Errors: NEOX_EINVAL (null), NEOX_EHIP. */
+/* Wait for the stream of the last call that enqueued work on this handle and copy the
+ * state to *out.  A step replayed from a captured HIP graph is not such a call: wait for
+ * the replay's stream before reading the state.  Errors: NEOX_EINVAL (null), NEOX_EHIP. */
 int neox_scaler_state(neox_zero1* h, neox_scaler_state_t* out);
 
 /* Wait for outstanding work and free the library's scratch (never caller memory).
+ * A graph that captured a step of this handle must not be replayed afterwards.
  * NULL is a no-op returning NEOX_OK. */
 int neox_zero1_destroy(neox_zero1* h);
 

@@ -349,6 +349,10 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
     h->nseg = (uint32_t)nseg;
     std::vector<uint32_t> seg_range;
+    if (cfg->segment_norms && nseg >= (1u << 24)) {
+        free_handle(h);
+        return fail(NEOX_EINVAL, "segment_norms supports fewer than 2^24 segments");
+    }
     if (cfg->segment_norms) {
         // norm chunks are built segment by segment, so each segment owns a contiguous range
         seg_range.assign(2 * nseg, 0);

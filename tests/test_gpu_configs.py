@@ -151,3 +151,14 @@ def test_opt_style_6b_collapse_and_recovery():
     chk = run(w, checked_steps={0, 38}, threads=16)
     st = chk.ost
     assert (st.skipped_total, st.step, st.loss_scale) == (20, 19, 16.0)
+
+
+def test_multi_tensor_literal_draws_138gb():
+    """The multi-tensor workload with its sizes drawn literally (5,000 tensors of
+    log-uniform 1K..16M elements, ~8.6e9 params, ~138 GB of resident state): decisions
+    every step, the oracle's full norm and sampled windows on the first and last steps."""
+    w = W.multi_tensor(steps=4, literal=True)
+    assert w.numel > 8e9
+    log(f"case multi-tensor literal: {w.numel} params")
+    chk = run(w, checked_steps={0, 3}, threads=16)
+    assert chk.ost.step == 4 and chk.ost.last_coef < 1.0

@@ -95,7 +95,7 @@ def pythia410m_tensors():
     return out
 
 
-def _layer_tensors(h, bias_ffn=True):
+def _layer_tensors(h):
     """One decoder layer of hidden size h in model order (LN1, QKV, out, LN2, FC, proj)."""
     return [(h, False), (h, False), (h * 3 * h, True), (3 * h, False), (h * h, True),
             (h, False), (h, False), (h, False), (h * 4 * h, True), (4 * h, False),
@@ -174,7 +174,8 @@ def multi_tensor(steps: int = 20, literal: bool = False, count: int = 5000,
     nodecay[rng.permutation(count)[: count // 5]] = True
     segs = [(int(k), not bool(nd)) for k, nd in zip(n, nodecay)]
     hy = Hyper(dtype=BF16, scaler_mode=STATIC, init_scale=1.0)
-    return Workload("multi_tensor_5000_bf16", 4, segs, hy, flat=False, steps=steps)
+    name = "multi_tensor_5000_bf16_literal" if literal else "multi_tensor_5000_bf16"
+    return Workload(name, 4, segs, hy, flat=False, steps=steps)
 
 
 def opt_large(numel: int = 6_000_000_000) -> Workload:
@@ -202,6 +203,7 @@ BENCH_WORKLOADS = {
     "pythia410m_dp8_rank0": lambda: pythia410m(0),
     "pythia410m_dp8_rank1": lambda: pythia410m(1),
     "multi_tensor_5000_bf16": multi_tensor,
+    "multi_tensor_5000_bf16_literal": lambda: multi_tensor(literal=True),
     "opt_style_6b": opt_large,
 }
 
