@@ -22,13 +22,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 UPDATE_BYTES_PER_PARAM = 28      # grad 2 + master/m/v 12 read; master/m/v 12 + half 2 written
 STEP_BYTES_PER_PARAM = 30        # + the norm pass's 2-byte gradient read
-KERNEL_SRC = os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", "zero1_kernels.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "update_kernel_neox20b_shard_215m_pmc.txt")
+# the sources that fix the kernels' code and launch shapes
+KERNEL_SRCS = tuple(os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
+                    for f in ("zero1_kernels.hip", "zero1_internal.h", "zero1_api.hip"))
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "flat_update_kernel_neox20b_shard_215m_pmc.txt")
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic(workload, n):
@@ -51,6 +56,60 @@ def read_traffic(workload, n):
         return None
 
 
+def summarize_trace(args):
+    """Write the kernel-time summary (profiles/...) from a rocprofv3 --kernel-trace --stats
+    run of this program, with the algorithmic bandwidth of the step's kernels and, given
+    that run's bench log, the HIP-event averages bench.py measured in the same process."""
+    import csv
+    import glob
+
+    import workloads as W
+    files = glob.glob(os.path.join(args.trace, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {args.trace}")
+    with open(files[0]) as fh:
+        rows = [r for r in csv.DictReader(fh) if "nz1::" in r["Name"]]
+    n = W.BENCH_WORKLOADS[args.workload]().numel
+    per_param = {"update_kernel": UPDATE_BYTES_PER_PARAM, "norm_kernel": 2}
+    lines = [
+        f"# rocprofv3 kernel trace of the ZeRO-1 step on {args.workload} ({n} params), MI355X (gfx950).",
+        "# Commands (repository root on the GPU box):",
+        f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py "
+        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline > <log>",
+        f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} --bench-log <log>",
+        f"# Calls = 3 warm-up + {args.trace_steps} timed steps (update-kernel events only) + 20 steps",
+        "# with events around every kernel; the torch kernels that draw the synthetic inputs and the",
+        "# ceiling probes are left out.  Durations in ns.",
+        f"kernel_source_sha256: {kernel_sha()}",
+        f"{'kernel':44s} {'calls':>6s} {'avg_ns':>10s} {'min_ns':>10s} {'max_ns':>10s}",
+    ]
+    rates = []
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("void ", "").split("(")[0]
+        lines.append(f"{name:44s} {int(r['Calls']):6d} {float(r['AverageNs']):10.0f} "
+                     f"{int(r['MinNs']):10d} {int(r['MaxNs']):10d}")
+        for k, bpp in per_param.items():
+            if name.split("<")[0].endswith(k):
+                us = float(r["AverageNs"]) / 1e3
+                rates.append(f"{name.split('<')[0]}: {bpp * n} algorithmic bytes per launch / "
+                             f"{us:.1f} us = {bpp * n / (us * 1e-6) / 1e9:.1f} GB/s")
+    lines += [""] + rates
+    if args.bench_log:
+        with open(args.bench_log) as fh:
+            last = [ln for ln in fh if ln.startswith("{")][-1]
+        b = json.loads(last)
+        k = b.get("kernel_avg_ms", {})
+        lines.append(f"bench.py in the same run (HIP events on the step's stream): update avg "
+                     f"{k.get('update', 0) * 1e3:.1f} us, norm {k.get('norm', 0) * 1e3:.1f} us, "
+                     f"finalize {k.get('finalize', 0) * 1e3:.1f} us, step "
+                     f"{b['ms_per_step'] * 1e3:.1f} us wall")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text, end="")
+
+
 def summarize_pmc(args):
     """Write the traffic summary bench.py reads (profiles/...) from rocprofv3 --pmc
     output: FETCH_SIZE and WRITE_SIZE of the update kernel, each scaled by what the same
@@ -67,12 +126,15 @@ def summarize_pmc(args):
             raise SystemExit(f"no counter_collection.csv under {d}")
         return out
 
+    names = set()
+
     def avg(d, counter, name_part):
-        vals = [float(r["Counter_Value"]) for r in rows(d)
-                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
-        if not vals:
+        sel = [r for r in rows(d) if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+        if not sel:
             raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} in {d}")
-        return sum(vals) / len(vals), len(vals)
+        if name_part == "update_kernel":
+            names.update(r["Kernel_Name"].replace("void ", "").split("(")[0] for r in sel)
+        return sum(float(r["Counter_Value"]) for r in sel) / len(sel), len(sel)
 
     fetch, nf = avg(args.pmc_fetch, "FETCH_SIZE", "update_kernel")
     write, nw = avg(args.pmc_write, "WRITE_SIZE", "update_kernel")
@@ -84,7 +146,7 @@ def summarize_pmc(args):
     n = W.BENCH_WORKLOADS[args.workload]().numel
     traffic = (fetch * ff + write * fw) * 1024.0
     lines = [
-        f"# HBM traffic of the update kernel on {args.workload} ({n} params), from rocprofv3 PMC.",
+        f"# HBM traffic of the update on {args.workload} ({n} params), from rocprofv3 PMC.",
         "# Commands (run from the repository root on the MI355X box):",
         f"#   rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- python3 bench.py "
         f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events",
@@ -99,6 +161,7 @@ def summarize_pmc(args):
         "# give the factors that turn counter KiB into bytes.  Counters count traffic leaving",
         "# the L2 (Infinity Cache hits included).",
         f"workload: {args.workload}",
+        f"kernel: {', '.join(sorted(names))}",
         f"kernel_source_sha256: {kernel_sha()}",
         f"update_dispatches: {nf}",
         f"fetch_kib_per_dispatch: {fetch:.1f}",
@@ -133,6 +196,11 @@ def copy_probe(nbytes):
     print(f"[bench] copy probe: 3 x {nbytes} bytes", file=sys.stderr, flush=True)
 
 
+# threads per block x vectors per thread / blocks per CU (0 = unlimited)
+PATTERN_SHAPES = ((256, 2, 0), (256, 2, 1), (256, 1, 1), (256, 1, 2), (128, 2, 1), (128, 2, 2),
+                  (64, 2, 4))
+
+
 def measure_ceiling(bufs, n, reps=20):
     """GB/s of the stream probes on the workload's own arrays (contents are clobbered)."""
     import torch
@@ -152,10 +220,18 @@ def measure_ceiling(bufs, n, reps=20):
         e1.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    ms_pat = timed(lambda: P.neox_probe_update_pattern(ptr["grad"], ptr["half"], ptr["master"],
-                                                       ptr["m"], ptr["v"], n, stream.cuda_stream))
+    # the pattern at several launch shapes (threads, vectors per thread, blocks per CU);
+    # the ceiling is the best of them
+    sweep = {}
+    for t, u, c in PATTERN_SHAPES:
+        ms = timed(lambda: P.neox_probe_update_pattern(ptr["grad"], ptr["half"], ptr["master"],
+                                                       ptr["m"], ptr["v"], n, t, u, c,
+                                                       stream.cuda_stream))
+        sweep[f"{t}x{u}/cu{c}"] = UPDATE_BYTES_PER_PARAM * n / (ms * 1e-3) / 1e9
+    best = max(sweep, key=sweep.get)
     ms_copy = timed(lambda: P.neox_probe_copy(ptr["master"], ptr["m"], 4 * n, stream.cuda_stream))
-    return {"update_pattern_gbps": UPDATE_BYTES_PER_PARAM * n / (ms_pat * 1e-3) / 1e9,
+    return {"update_pattern_gbps": sweep[best], "update_pattern_shape": best,
+            "update_pattern_sweep": {k: round(v, 1) for k, v in sweep.items()},
             "copy_gbps": 8 * n / (ms_copy * 1e-3) / 1e9}
 
 
@@ -215,6 +291,8 @@ def main():
                     help="time the split step (step_local + step_apply on the local value)")
     ap.add_argument("--segment-norms", action="store_true",
                     help="keep per-segment squared norms (telemetry) during the step")
+    ap.add_argument("--chunked-update", action="store_true",
+                    help="run the update from the per-chunk work table even on a flat shard")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--no-timing-events", action="store_true",
@@ -223,6 +301,10 @@ def main():
                     help="run only a plain streaming copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-pmc", action="store_true",
                     help="write the update kernel's traffic summary from rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-trace", metavar="DIR", dest="trace",
+                    help="write the kernel-time summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--trace-steps", type=int, default=20)
+    ap.add_argument("--bench-log")
     ap.add_argument("--pmc-fetch")
     ap.add_argument("--pmc-write")
     ap.add_argument("--pmc-copy-fetch")
@@ -232,6 +314,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.trace:
+        summarize_trace(args)
         return
     if args.copy_probe_only:
         copy_probe(args.copy_probe_only)
@@ -296,7 +381,9 @@ def main():
         dtype=w.hyper.dtype, scaler_mode=w.hyper.scaler_mode,
         growth_interval=w.hyper.growth_interval, init_scale=w.hyper.init_scale,
         min_scale=w.hyper.min_scale, optimizer=w.hyper.optimizer,
-        segment_norms=int(args.segment_norms)), segs, stream.cuda_stream)
+        segment_norms=int(args.segment_norms), chunked_update=int(args.chunked_update)),
+        segs, stream.cuda_stream)
+    flat_path = Z.neox_zero1_update_path(h) == Z.NEOX_PATH_FLAT
     loc = torch.zeros(1, dtype=torch.float64, device=dev)
 
     def one_step():
@@ -368,7 +455,8 @@ def main():
                    "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
                    "layout": "flat shard" if w.flat else "separate allocations",
                    "optimizer": args.optimizer, "split": args.split,
-                   "segment_norms": args.segment_norms, "graph": args.graph},
+                   "segment_norms": args.segment_norms, "graph": args.graph,
+                   "update_path": "flat" if flat_path else "chunked"},
         "hbm": {"step_bytes": step_bpp * n,
                 "step_gbps": step_bpp * n / (ms_per_step * 1e-3) / 1e9,
                 "step_frac_of_peak": step_bpp * n / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -379,13 +467,16 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": upd_gbs / HBM_PEAK_GBS,
                            "traffic": read_traffic(w.name, n) if default_mode else None,
-                           "kernel": "update_kernel", "avg_ms": kernel_ms[2],
+                           "kernel": "flat_update_kernel" if flat_path else "update_kernel",
+                           "avg_ms": kernel_ms[2],
                            "bytes_per_launch": upd_bpp * n}
         out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],
                                 "update": kernel_ms[2]}
     if ceiling:
         ceiling["note"] = ("measured on this GPU right after the timed steps: a kernel with the "
-                           "update's exact access pattern and trivial arithmetic, and a plain copy")
+                           "update's access pattern and trivial arithmetic, best of the launch "
+                           "shapes swept (threads x vectors per thread / blocks per CU), and a "
+                           "plain copy")
         if kernel_ms:
             ceiling["update_kernel_frac_of_pattern"] = out["roofline"]["achieved"] / \
                 ceiling["update_pattern_gbps"]

@@ -23,10 +23,14 @@ int neox_probe_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream
 
 /* The update kernel's memory access pattern with trivial arithmetic: over n elements
  * (a multiple of 8) it reads a 2-byte gradient and three FP32 arrays and writes the
- * three FP32 arrays in place and a 2-byte copy, 28 bytes per element, in the same
- * 4096-element blocks, order and vector width.  The arrays' contents are changed. */
+ * three FP32 arrays in place and a 2-byte copy, 28 bytes per element, with 16-byte
+ * vectors, in tiles walked last-to-first.  Launch shape: `threads` per block (64, 128,
+ * 256 or 512), `vectors` 8-element vectors per thread (1, 2 or 4; a tile is threads x
+ * vectors x 8 elements), at most `blocks_per_cu` blocks per CU (0 = as many as fit;
+ * 1..16, enforced by reserving LDS).  The arrays' contents are changed. */
 int neox_probe_update_pattern(const void* grad, void* half, float* master, float* exp_avg,
-                              float* exp_avg_sq, uint64_t n, void* hip_stream);
+                              float* exp_avg_sq, uint64_t n, int32_t threads, int32_t vectors,
+                              int32_t blocks_per_cu, void* hip_stream);
 
 const char* neox_probe_last_error(void);
 

@@ -55,6 +55,9 @@ extern "C" {
 #define NEOX_OPT_ADAMW 0         /* Adam with bias correction, decoupled decay   */
 #define NEOX_OPT_SGD   1         /* heavy-ball momentum SGD, decoupled decay     */
 
+#define NEOX_PATH_CHUNKED 0     /* update driven by the per-chunk work table    */
+#define NEOX_PATH_FLAT    1     /* update addresses a flat partition's tiles    */
+
 #define NEOX_SEG_DECAY 1u       /* segment receives decoupled weight decay      */
 #define NEOX_PAD_TENSOR 0xFFFFFFFFu
 
@@ -94,6 +97,13 @@ typedef struct neox_zero1_config {
      * (neox_zero1_segment_sumsq); needs norm_blocks == 0.  Gradient-norm spikes per
      * tensor are how the OPT card (瓶颈, 方法适配) diagnoses instability. */
     uint32_t segment_norms;
+    /* Update kernel.  0: when chunk_elems is 0 and the segments, in order, tile five
+     * contiguous arrays whose first elements are 16-byte aligned (one flat ZeRO-1
+     * partition, as neox_zero1_partition lays it out), the update computes each tile's
+     * addresses from its index and loads its data without first reading a work
+     * descriptor; any other layout uses the per-chunk work table.  1: always the work
+     * table.  Results do not depend on the choice. */
+    uint32_t chunked_update;
 } neox_zero1_config;
 
 /* One contiguous run of parameters of the shard, with its five device arrays, each
@@ -181,8 +191,10 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
 /* Enqueue one step on hip_stream and return without waiting: a norm/overflow pass
  * over every gradient, a one-block finalize (skip decision, clip coefficient, step
  * count, bias corrections, loss-scale update, all on the device), and the fused
- * unscale + clip + AdamW + cast update, which returns at once when the finalize
- * decided to skip.  The gradient must be complete in stream order before this call.
+ * unscale + clip + AdamW + cast update, which writes nothing when the finalize decided
+ * to skip (the chunked update then returns at once; the flat one has already issued
+ * its tile's loads and drops them).  The gradient must be complete in stream order
+ * before this call.
  * On a skipped step master, exp_avg, exp_avg_sq and half are not written.
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
 int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream);
@@ -237,6 +249,10 @@ int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg);
  * Errors: NEOX_EINVAL, NEOX_ENOMEM, NEOX_EHIP. */
 int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only);
 int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);
+
+/* Which update kernel the handle runs: NEOX_PATH_FLAT or NEOX_PATH_CHUNKED (see
+ * chunked_update).  Errors: NEOX_EINVAL (null handle). */
+int neox_zero1_update_path(const neox_zero1* h);
 
 /* Text of the last error raised on the calling thread (never NULL). */
 const char* neox_zero1_last_error(void);

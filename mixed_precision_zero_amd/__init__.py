@@ -19,6 +19,7 @@ NEOX_OK, NEOX_EINVAL, NEOX_EHIP, NEOX_ENOMEM = 0, -1, -2, -3
 NEOX_F16, NEOX_BF16 = 1, 2
 NEOX_SCALER_DYNAMIC, NEOX_SCALER_STATIC = 0, 1
 NEOX_OPT_ADAMW, NEOX_OPT_SGD = 0, 1
+NEOX_PATH_CHUNKED, NEOX_PATH_FLAT = 0, 1
 NEOX_SEG_DECAY = 1
 NEOX_PAD_TENSOR = 0xFFFFFFFF
 
@@ -40,7 +41,7 @@ class neox_zero1_config(C.Structure):
                 ("init_skipped", C.c_int64), ("init_good_steps", C.c_int32),
                 ("init_consecutive_overflows", C.c_int32), ("chunk_elems", C.c_uint32),
                 ("norm_blocks", C.c_uint32), ("optimizer", C.c_int32),
-                ("segment_norms", C.c_uint32)]
+                ("segment_norms", C.c_uint32), ("chunked_update", C.c_uint32)]
 
 
 class neox_segment(C.Structure):
@@ -67,7 +68,8 @@ EXPORTS = ("neox_zero1_default_config", "neox_zero1_partition", "neox_zero1_crea
            "neox_zero1_step", "neox_scaler_state", "neox_zero1_destroy",
            "neox_zero1_step_local", "neox_zero1_step_apply", "neox_scaler_set",
            "neox_zero1_segment_sumsq",
-           "neox_zero1_timing_begin", "neox_zero1_timing_end", "neox_zero1_last_error")
+           "neox_zero1_timing_begin", "neox_zero1_timing_end", "neox_zero1_update_path",
+           "neox_zero1_last_error")
 
 _lib = None
 
@@ -96,6 +98,7 @@ def lib():
         L.neox_zero1_segment_sumsq.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64]
         L.neox_zero1_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
         L.neox_zero1_timing_end.argtypes = [C.c_void_p, P(C.c_double), P(C.c_int64)]
+        L.neox_zero1_update_path.argtypes = [C.c_void_p]
         L.neox_zero1_last_error.argtypes = []
         L.neox_zero1_last_error.restype = C.c_char_p
         for name in EXPORTS:
@@ -197,6 +200,14 @@ def neox_zero1_segment_sumsq(h: int, nseg: int):
 
 def neox_zero1_timing_begin(h: int, max_steps: int, update_only: bool = False):
     _check(lib().neox_zero1_timing_begin(C.c_void_p(h), max_steps, int(update_only)))
+
+
+def neox_zero1_update_path(h: int) -> int:
+    """NEOX_PATH_FLAT or NEOX_PATH_CHUNKED: which update kernel the handle runs."""
+    rc = lib().neox_zero1_update_path(C.c_void_p(h))
+    if rc < 0:
+        _check(rc)
+    return rc
 
 
 def neox_zero1_timing_end(h: int):

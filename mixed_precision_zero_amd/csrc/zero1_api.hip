@@ -50,6 +50,9 @@ int hip_fail(hipError_t e, const char* what) {
 #ifndef NZ1_NORM_BLOCKS_PER_CU
 #define NZ1_NORM_BLOCKS_PER_CU 0
 #endif
+#ifndef NZ1_FLAT_BLOCKS_PER_CU
+#define NZ1_FLAT_BLOCKS_PER_CU 2
+#endif
 constexpr uint32_t kDefaultChunk = NZ1_UPDATE_CHUNK;
 constexpr uint32_t kNormChunk = NZ1_NORM_CHUNK;
 
@@ -67,6 +70,11 @@ struct neox_zero1 {
     uint32_t norm_blocks = 0;
     uint32_t update_lds = 0;       // LDS reserved per update block (occupancy cap)
     uint32_t norm_lds = 0;         // LDS reserved per norm block
+    uint32_t flat_lds = 0;         // LDS reserved per flat-update block
+    bool flat = false;             // update runs flat_update_kernel over `span`
+    FlatSpan span{};
+    uint32_t* d_tile_word = nullptr;
+    uint32_t* d_change = nullptr;
     Chunk* d_chunks = nullptr;
     Chunk* d_norm_chunks = nullptr;
     uint32_t nseg = 0;
@@ -140,6 +148,7 @@ static int validate_config(const neox_zero1_config* c) {
     if (c->optimizer != NEOX_OPT_ADAMW && c->optimizer != NEOX_OPT_SGD)
         return fail(NEOX_EINVAL, "optimizer %d", c->optimizer);
     if (c->segment_norms > 1) return fail(NEOX_EINVAL, "segment_norms %u", c->segment_norms);
+    if (c->chunked_update > 1) return fail(NEOX_EINVAL, "chunked_update %u", c->chunked_update);
     if (c->segment_norms && c->norm_blocks)
         return fail(NEOX_EINVAL, "segment_norms needs the one-block-per-chunk norm pass (norm_blocks 0)");
     return NEOX_OK;
@@ -246,6 +255,55 @@ static void build_chunks(const neox_segment* segs, uint64_t nseg, uint32_t C, st
     }
 }
 
+// The segments, in order, tile five contiguous arrays (exp_avg_sq too when has_v)
+// whose first elements are 16-byte aligned: one flat partition.  *n gets its length.
+static bool flat_layout(const neox_segment* segs, uint64_t nseg, bool has_v, uint64_t* n) {
+    const neox_segment& s0 = segs[0];
+    if (!aligned16((uintptr_t)s0.grad) || !aligned16((uintptr_t)s0.half) ||
+        !aligned16((uintptr_t)s0.master) || !aligned16((uintptr_t)s0.exp_avg) ||
+        (has_v && !aligned16((uintptr_t)s0.exp_avg_sq)))
+        return false;
+    uint64_t off = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        const neox_segment& s = segs[k];
+        if ((uintptr_t)s.grad != (uintptr_t)s0.grad + 2 * off ||
+            (uintptr_t)s.half != (uintptr_t)s0.half + 2 * off ||
+            (uintptr_t)s.master != (uintptr_t)s0.master + 4 * off ||
+            (uintptr_t)s.exp_avg != (uintptr_t)s0.exp_avg + 4 * off ||
+            (has_v && (uintptr_t)s.exp_avg_sq != (uintptr_t)s0.exp_avg_sq + 4 * off))
+            return false;
+        off += s.numel;
+    }
+    *n = off;
+    return true;
+}
+
+// Per-tile decay description of a flat partition of n elements: word[T] = (index in
+// `change` of tile T's first in-tile flag change) << 1 | flag of the tile's first
+// element; word[ntiles] closes the last list; change holds in-tile offsets.
+static void build_flat_tables(const neox_segment* segs, uint64_t nseg, uint64_t n,
+                              std::vector<uint32_t>& word, std::vector<uint32_t>& change) {
+    std::vector<uint64_t> at;   // element indices where the decay flag differs from the previous one
+    uint64_t off = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        if (k && (segs[k].flags & NEOX_SEG_DECAY) != (segs[k - 1].flags & NEOX_SEG_DECAY))
+            at.push_back(off);
+        off += segs[k].numel;
+    }
+    const uint64_t ntiles = (n + kFlatTile - 1) / kFlatTile;
+    word.assign(ntiles + 1, 0);
+    change.clear();
+    uint32_t flag = (segs[0].flags & NEOX_SEG_DECAY) ? 1u : 0u;
+    size_t j = 0;
+    for (uint64_t T = 0; T < ntiles; ++T) {
+        const uint64_t lo = T * kFlatTile, hi = lo + kFlatTile;
+        for (; j < at.size() && at[j] <= lo; ++j) flag ^= 1u;
+        word[T] = (uint32_t)(change.size() << 1) | flag;
+        for (size_t k = j; k < at.size() && at[k] < hi; ++k) change.push_back((uint32_t)(at[k] - lo));
+    }
+    word[ntiles] = (uint32_t)(change.size() << 1);
+}
+
 static bool overlaps(uintptr_t a, uint64_t abytes, uintptr_t b, uint64_t bbytes) {
     return a < b + bbytes && b < a + abytes;
 }
@@ -296,6 +354,8 @@ static void free_handle(neox_zero1* h) {
     if (h->d_seg_sumsq) (void)hipFree(h->d_seg_sumsq);
     if (h->d_partial) (void)hipFree(h->d_partial);
     if (h->d_state) (void)hipFree(h->d_state);
+    if (h->d_tile_word) (void)hipFree(h->d_tile_word);
+    if (h->d_change) (void)hipFree(h->d_change);
     delete h;
 }
 
@@ -323,6 +383,21 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     }
     if (table.size() >= (1ull << 24)) return fail(NEOX_EINVAL, "%zu chunks: raise chunk_elems", table.size());
 
+    const bool has_v = cfg->optimizer == NEOX_OPT_ADAMW;
+    uint64_t flat_n = 0;
+    const bool flat = !cfg->chunked_update && cfg->chunk_elems == 0 &&
+                      flat_layout(segs, nseg, has_v, &flat_n) &&
+                      // the grid's x size in work-items is 32-bit
+                      (flat_n + kFlatTile - 1) / kFlatTile * kFlatBlock < (1ull << 32);
+    std::vector<uint32_t> tile_word, change;
+    if (flat) {
+        try {
+            build_flat_tables(segs, nseg, flat_n, tile_word, change);
+        } catch (const std::bad_alloc&) {
+            return fail(NEOX_ENOMEM, "host allocation of the tile table");
+        }
+    }
+
     neox_zero1* h = new (std::nothrow) neox_zero1();
     if (!h) return fail(NEOX_ENOMEM, "host allocation of the handle");
     h->cfg = *cfg;
@@ -340,6 +415,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     };
     h->update_lds = reserve(NZ1_UPDATE_BLOCKS_PER_CU);
     h->norm_lds = reserve(NZ1_NORM_BLOCKS_PER_CU);
+    h->flat_lds = reserve(NZ1_FLAT_BLOCKS_PER_CU);
     h->nnorm = (uint32_t)norm_table.size();
     // norm pass: one block per norm chunk unless a smaller striding grid is requested
     uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : h->nnorm;
@@ -369,6 +445,8 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_sumsq, nseg * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_partial, nb * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_state, sizeof(DevState));
+    if (e == hipSuccess && flat) e = hipMalloc(&h->d_tile_word, tile_word.size() * sizeof(uint32_t));
+    if (e == hipSuccess && flat) e = hipMalloc(&h->d_change, (change.size() + 1) * sizeof(uint32_t));
     if (e != hipSuccess) {
         free_handle(h);
         return e == hipErrorOutOfMemory ? fail(NEOX_ENOMEM, "hipMalloc of library scratch")
@@ -396,6 +474,12 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
         e = hipMemcpyAsync(h->d_seg_range, seg_range.data(), seg_range.size() * sizeof(uint32_t),
                            hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(h->d_state, &st, sizeof st, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess && flat)
+        e = hipMemcpyAsync(h->d_tile_word, tile_word.data(), tile_word.size() * sizeof(uint32_t),
+                           hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess && flat && !change.empty())
+        e = hipMemcpyAsync(h->d_change, change.data(), change.size() * sizeof(uint32_t),
+                           hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) { free_handle(h); return hip_fail(e, "upload of the chunk table"); }
 
@@ -410,6 +494,20 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     f.min_scale = (float)cfg->min_scale;
     f.dynamic = cfg->scaler_mode == NEOX_SCALER_DYNAMIC;
     f.growth_interval = cfg->growth_interval;
+
+    if (flat) {
+        h->flat = true;
+        FlatSpan& sp = h->span;
+        sp.grad = static_cast<const uint16_t*>(segs[0].grad);
+        sp.half = static_cast<uint16_t*>(segs[0].half);
+        sp.master = segs[0].master;
+        sp.m = segs[0].exp_avg;
+        sp.v = has_v ? segs[0].exp_avg_sq : nullptr;
+        sp.n = flat_n;
+        sp.tile_word = h->d_tile_word;
+        sp.change = h->d_change;
+        sp.ntiles = (uint32_t)(tile_word.size() - 1);
+    }
 
     UpdateArgs& u = h->upd_base;
     u.b1 = (float)cfg->beta1;
@@ -437,6 +535,9 @@ static hipError_t enqueue_norm(neox_zero1* h, hipStream_t stream) {
 static hipError_t enqueue_update(neox_zero1* h, float lr, hipStream_t stream) {
     UpdateArgs u = h->upd_base;
     u.lr = lr;
+    if (h->flat)
+        return launch_flat_update(h->cfg.dtype, h->cfg.optimizer, h->span, h->d_state, u,
+                                  h->flat_lds, stream);
     return launch_update(h->cfg.dtype, h->cfg.optimizer, h->d_chunks, h->nchunks, h->d_state, u,
                          h->update_lds, stream);
 }
@@ -582,6 +683,11 @@ extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* st
     h->timing.clear();
     h->timing_used = 0;
     return NEOX_OK;
+}
+
+extern "C" int neox_zero1_update_path(const neox_zero1* h) {
+    if (!h) return fail(NEOX_EINVAL, "handle is NULL");
+    return h->flat ? NEOX_PATH_FLAT : NEOX_PATH_CHUNKED;
 }
 
 extern "C" const char* neox_zero1_last_error(void) { return g_last_error.c_str(); }

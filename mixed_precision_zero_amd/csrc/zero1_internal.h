@@ -56,6 +56,34 @@ struct alignas(64) DevState {
 };
 static_assert(offsetof(DevState, skip) % 16 == 0, "update fields share one 16-byte load");
 
+// Flat layout: the segments, in order, tile five contiguous arrays whose first elements
+// are 16-byte aligned.  Work unit: one tile of kFlatTile elements per block.  Measured
+// best on MI355X: 128 threads x 2 vectors (2,048-element tiles) at 2 blocks per CU;
+// fewer tiles in flight per CU keep the chip's open DRAM rows few, and the block's
+// single round trip keeps that low occupancy from exposing latency.
+#ifndef NZ1_FLAT_BLOCK
+#define NZ1_FLAT_BLOCK 128
+#endif
+#ifndef NZ1_FLAT_UNROLL
+#define NZ1_FLAT_UNROLL 2
+#endif
+constexpr int kFlatBlock = NZ1_FLAT_BLOCK;                       // threads per block
+constexpr int kFlatUnroll = NZ1_FLAT_UNROLL;                     // thread-vectors per thread
+constexpr uint32_t kFlatTile = kFlatBlock * kFlatUnroll * kVec;  // elements per block
+struct FlatSpan {
+    const uint16_t* grad;
+    uint16_t* half;
+    float* master;
+    float* m;
+    float* v;                      // null for momentum SGD
+    uint64_t n;                    // elements
+    // ntiles + 1 words: bit 0 = decay flag of the tile's first element, bits 1.. = index
+    // in `change` of the tile's first flag change; word T+1 ends tile T's list
+    const uint32_t* tile_word;
+    const uint32_t* change;        // in-tile offsets (1 .. kFlatTile-1) where the flag flips
+    uint32_t ntiles;
+};
+
 struct FinalizeArgs {
     double clip_norm;
     double beta1, beta2;
@@ -86,6 +114,8 @@ hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64
 hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
                          const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
                          hipStream_t stream);
+hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const DevState* st,
+                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream);
 
 // The unscale factor for scale s, computed in double and rounded once to FP32; the
 // host (initial state) and the finalize kernel evaluate the same expression.

@@ -369,12 +369,91 @@ __device__ __forceinline__ void adam(float h, float& w, float& m, float& v, cons
     w = __builtin_fmaf(-a.lr, u, w);
 }
 
+// One thread-vector: 8 consecutive elements whose gradient, master, m and v are already
+// in registers; updates them, stores the FP32 state and the half copy.  Bit e of dmask
+// set: element e receives decoupled weight decay.
+template <int DT, int OPT>
+__device__ __forceinline__ void update8(const uint4& G, const float4 (&W)[2], const float4 (&M)[2],
+                                        const float4 (&V)[2], const Coefs& c, const UpdateArgs& a,
+                                        uint32_t dmask, uint4* __restrict__ h4,
+                                        float4* __restrict__ w4, float4* __restrict__ m4,
+                                        float4* __restrict__ v4, uint64_t i) {
+    constexpr bool ADAM = OPT == 0;
+    const uint32_t gw[4] = {G.x, G.y, G.z, G.w};
+    float w[8] = {W[0].x, W[0].y, W[0].z, W[0].w, W[1].x, W[1].y, W[1].z, W[1].w};
+    float m[8] = {M[0].x, M[0].y, M[0].z, M[0].w, M[1].x, M[1].y, M[1].z, M[1].w};
+    float v[8];
+    if constexpr (ADAM) {
+        v[0] = V[0].x; v[1] = V[0].y; v[2] = V[0].z; v[3] = V[0].w;
+        v[4] = V[1].x; v[5] = V[1].y; v[6] = V[1].z; v[7] = V[1].w;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const bool d0 = (dmask >> (2 * k)) & 1u, d1 = (dmask >> (2 * k + 1)) & 1u;
+        if constexpr (ADAM) {
+            adam(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], v[2 * k], c, a, d0);
+            adam(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], v[2 * k + 1], c, a, d1);
+        } else {
+            sgd(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], c, a, d0);
+            sgd(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], c, a, d1);
+        }
+    }
+    constexpr bool NTS = NZ1_UPDATE_NT_STORE;
+    st16<NTS>(w4 + 2 * i, make_float4(w[0], w[1], w[2], w[3]));
+    st16<NTS>(w4 + 2 * i + 1, make_float4(w[4], w[5], w[6], w[7]));
+    st16<NTS>(m4 + 2 * i, make_float4(m[0], m[1], m[2], m[3]));
+    st16<NTS>(m4 + 2 * i + 1, make_float4(m[4], m[5], m[6], m[7]));
+    if constexpr (ADAM) {
+        st16<NTS>(v4 + 2 * i, make_float4(v[0], v[1], v[2], v[3]));
+        st16<NTS>(v4 + 2 * i + 1, make_float4(v[4], v[5], v[6], v[7]));
+    }
+    st16<NTS>(h4 + i, make_uint4(Fmt<DT>::pack(w[0], w[1]), Fmt<DT>::pack(w[2], w[3]),
+                                 Fmt<DT>::pack(w[4], w[5]), Fmt<DT>::pack(w[6], w[7])));
+}
+
+// One element on the scalar path.
+template <int DT, int OPT>
+__device__ __forceinline__ void update1(const uint16_t* __restrict__ gp, uint16_t* __restrict__ hp,
+                                        float* __restrict__ wp, float* __restrict__ mp,
+                                        float* __restrict__ vp, uint64_t i, const Coefs& c,
+                                        const UpdateArgs& a, bool decay) {
+    float w = wp[i], m = mp[i];
+    if constexpr (OPT == 0) {
+        float v = vp[i];
+        adam(Fmt<DT>::one(gp[i]), w, m, v, c, a, decay);
+        vp[i] = v;
+    } else {
+        sgd(Fmt<DT>::one(gp[i]), w, m, c, a, decay);
+    }
+    wp[i] = w;
+    mp[i] = m;
+    hp[i] = Fmt<DT>::enc(w);
+}
+
+// Loads of thread-vector i (8 elements) of the five arrays.
+template <int OPT>
+__device__ __forceinline__ void load8(const uint4* __restrict__ g4, const float4* __restrict__ w4,
+                                      const float4* __restrict__ m4, const float4* __restrict__ v4,
+                                      uint64_t i, uint4& G, float4 (&W)[2], float4 (&M)[2],
+                                      float4 (&V)[2]) {
+    constexpr bool NTL = NZ1_UPDATE_NT_LOAD;
+    G = ld16<NTL>(g4 + i);
+    W[0] = ld16<NTL>(w4 + 2 * i);
+    W[1] = ld16<NTL>(w4 + 2 * i + 1);
+    M[0] = ld16<NTL>(m4 + 2 * i);
+    M[1] = ld16<NTL>(m4 + 2 * i + 1);
+    if constexpr (OPT == 0) {
+        V[0] = ld16<NTL>(v4 + 2 * i);
+        V[1] = ld16<NTL>(v4 + 2 * i + 1);
+    }
+}
+
+// Generic layout: one block per entry of the chunk table.
 template <int DT, int U, int OPT>
 __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict__ chunks,
                                                         uint32_t nchunks,
                                                         const DevState* __restrict__ st,
                                                         UpdateArgs a) {
-    constexpr bool ADAM = OPT == 0;
     // NZ1_UPDATE_REVERSE walks the chunks last-to-first, so the first gradients the
     // update reads are the ones the norm pass read last.
     const Chunk* ch = chunks + (NZ1_UPDATE_REVERSE ? nchunks - 1 - blockIdx.x : blockIdx.x);
@@ -395,7 +474,7 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
     const uint32_t odd = (uint32_t)(((uintptr_t)gp | (uintptr_t)hp | (uintptr_t)wp |
                                      (uintptr_t)mp | (uintptr_t)vp) & 1u) | (flags >> 31);
     if (skip | (len == 0) | odd) return;
-    const bool decay = (flags & CH_DECAY) != 0;
+    const uint32_t dmask = (flags & CH_DECAY) ? 0xFFu : 0u;
 
     uint32_t done = 0;
     if (flags & CH_VEC) {
@@ -411,72 +490,156 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = base + u * kBlock + threadIdx.x;
-                if (i < nvec) {
-                    G[u] = ld16<NZ1_UPDATE_NT_LOAD>(g4 + i);
-                    W[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(w4 + 2 * i);
-                    W[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(w4 + 2 * i + 1);
-                    M[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(m4 + 2 * i);
-                    M[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(m4 + 2 * i + 1);
-                    if constexpr (ADAM) {
-                        V[u][0] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i);
-                        V[u][1] = ld16<NZ1_UPDATE_NT_LOAD>(v4 + 2 * i + 1);
-                    }
-                }
+                if (i < nvec) load8<OPT>(g4, w4, m4, v4, i, G[u], W[u], M[u], V[u]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t i = base + u * kBlock + threadIdx.x;
-                if (i < nvec) {
-                    const uint32_t gw[4] = {G[u].x, G[u].y, G[u].z, G[u].w};
-                    float w[8] = {W[u][0].x, W[u][0].y, W[u][0].z, W[u][0].w,
-                                  W[u][1].x, W[u][1].y, W[u][1].z, W[u][1].w};
-                    float m[8] = {M[u][0].x, M[u][0].y, M[u][0].z, M[u][0].w,
-                                  M[u][1].x, M[u][1].y, M[u][1].z, M[u][1].w};
-                    float v[8];
-                    if constexpr (ADAM) {
-                        v[0] = V[u][0].x; v[1] = V[u][0].y; v[2] = V[u][0].z; v[3] = V[u][0].w;
-                        v[4] = V[u][1].x; v[5] = V[u][1].y; v[6] = V[u][1].z; v[7] = V[u][1].w;
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        if constexpr (ADAM) {
-                            adam(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], v[2 * k], c, a, decay);
-                            adam(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], v[2 * k + 1], c,
-                                 a, decay);
-                        } else {
-                            sgd(Fmt<DT>::lo(gw[k]), w[2 * k], m[2 * k], c, a, decay);
-                            sgd(Fmt<DT>::hi(gw[k]), w[2 * k + 1], m[2 * k + 1], c, a, decay);
-                        }
-                    }
-                    constexpr bool NTS = NZ1_UPDATE_NT_STORE;
-                    st16<NTS>(w4 + 2 * i, make_float4(w[0], w[1], w[2], w[3]));
-                    st16<NTS>(w4 + 2 * i + 1, make_float4(w[4], w[5], w[6], w[7]));
-                    st16<NTS>(m4 + 2 * i, make_float4(m[0], m[1], m[2], m[3]));
-                    st16<NTS>(m4 + 2 * i + 1, make_float4(m[4], m[5], m[6], m[7]));
-                    if constexpr (ADAM) {
-                        st16<NTS>(v4 + 2 * i, make_float4(v[0], v[1], v[2], v[3]));
-                        st16<NTS>(v4 + 2 * i + 1, make_float4(v[4], v[5], v[6], v[7]));
-                    }
-                    st16<NTS>(h4 + i, make_uint4(Fmt<DT>::pack(w[0], w[1]), Fmt<DT>::pack(w[2], w[3]),
-                                                 Fmt<DT>::pack(w[4], w[5]), Fmt<DT>::pack(w[6], w[7])));
-                }
+                if (i < nvec) update8<DT, OPT>(G[u], W[u], M[u], V[u], c, a, dmask, h4, w4, m4, v4, i);
             }
         }
         done = nvec * kVec;
     }
     // scalar path: chunks that are not 16-byte aligned, and the last < 8 elements
-    for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
-        float w = wp[i], m = mp[i];
-        if constexpr (ADAM) {
-            float v = vp[i];
-            adam(Fmt<DT>::one(gp[i]), w, m, v, c, a, decay);
-            vp[i] = v;
-        } else {
-            sgd(Fmt<DT>::one(gp[i]), w, m, c, a, decay);
+    for (uint32_t i = done + threadIdx.x; i < len; i += kBlock)
+        update1<DT, OPT>(gp, hp, wp, mp, vp, i, c, a, (flags & CH_DECAY) != 0);
+}
+
+// Decay bits of the n <= 8 consecutive elements starting at offset o of a tile: the
+// tile's starting flag, flipped at each of the tile's change offsets that is <= the
+// element's offset.  change[first, end) is uniform across the block.
+__device__ __forceinline__ uint32_t decay_bits(const uint32_t* __restrict__ change, uint32_t first,
+                                               uint32_t end, uint32_t o, uint32_t start_mask) {
+    uint32_t mask = start_mask;
+    for (uint32_t j = first; j < end; ++j) {
+        const int d = (int)change[j] - (int)o;
+        if (d <= 0) mask ^= 0xFFu;
+        else if (d < kVec) mask ^= (0xFFu << d) & 0xFFu;
+    }
+    return mask;
+}
+
+// Uses loaded values (register operands of an empty asm).  Placed on the skip branch,
+// it gives the loads a user on both sides of that branch, so the compiler cannot sink
+// them below it: they stay in flight while the block waits for the decision.
+template <int OPT>
+__device__ __forceinline__ void keep_loaded(const uint4& G, const float4 (&W)[2],
+                                            const float4 (&M)[2], const float4 (&V)[2]) {
+    asm volatile("" ::"v"(G.x), "v"(W[0].x), "v"(W[1].x), "v"(M[0].x), "v"(M[1].x));
+    if constexpr (OPT == 0) asm volatile("" ::"v"(V[0].x), "v"(V[1].x));
+}
+
+// What a flat-update block reads besides its data: the finalize's decision and
+// coefficients, and its tile's two decay words.  Read with relaxed atomic loads: those
+// are vector-memory loads, which return in issue order, and the compiler keeps them in
+// program order after the data loads, so the block issues its whole tile before it
+// waits for anything.  (Plain loads of these uniform values would become scalar loads,
+// whose out-of-order completion makes the compiler wait for all of them before the data
+// loads go out.)  Workgroup scope suffices: the values were written by an earlier
+// kernel, complete before this one started.
+struct StepWords {
+    int32_t skip;
+    float gscale, rbc1, rsbc2;
+    uint32_t w0, w1;
+};
+__device__ __forceinline__ StepWords ld_after(const DevState* st, const uint32_t* word) {
+    const uint64_t a = __hip_atomic_load(reinterpret_cast<const uint64_t*>(&st->skip),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t b = __hip_atomic_load(reinterpret_cast<const uint64_t*>(&st->rbc1),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    StepWords r;
+    r.skip = (int32_t)(uint32_t)a;
+    r.gscale = __uint_as_float((uint32_t)(a >> 32));
+    r.rbc1 = __uint_as_float((uint32_t)b);
+    r.rsbc2 = __uint_as_float((uint32_t)(b >> 32));
+    r.w0 = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    r.w1 = __hip_atomic_load(word + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return r;
+}
+
+// Flat layout: the segments tile five contiguous 16-byte-aligned arrays (a flat
+// partition), so tile T's addresses follow from T alone.  A block issues its data loads
+// together with the fetch of its tile's decay words and of the finalize's decision,
+// instead of waiting for a work descriptor before its first data load.  On a skipped
+// step the tile is read and dropped; nothing is written.
+template <int DT, int OPT>
+__global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
+                                                             const uint32_t* __restrict__ tile_word,
+                                                             const uint32_t* __restrict__ change,
+                                                             const DevState* __restrict__ st,
+                                                             UpdateArgs a) {
+    constexpr int U = kFlatUnroll;
+    const uint32_t T = s.ntiles - 1 - blockIdx.x;     // last tile first, as above
+    const uint64_t nvec = s.n / kVec;
+    const uint64_t v0 = (uint64_t)T * (U * kFlatBlock);
+    const uint4* __restrict__ g4 = reinterpret_cast<const uint4*>(s.grad);
+    uint4* __restrict__ h4 = reinterpret_cast<uint4*>(s.half);
+    float4* __restrict__ w4 = reinterpret_cast<float4*>(s.master);
+    float4* __restrict__ m4 = reinterpret_cast<float4*>(s.m);
+    float4* __restrict__ v4 = reinterpret_cast<float4*>(s.v);
+
+    if (T + 1 < s.ntiles || s.n % kFlatTile == 0) {
+        // a full tile: every thread owns U whole vectors
+        uint4 G[U];
+        float4 W[U][2], M[U][2], V[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            load8<OPT>(g4, w4, m4, v4, v0 + u * kFlatBlock + threadIdx.x, G[u], W[u], M[u], V[u]);
+        // Then the decision, the coefficients and the tile words, as vector loads issued
+        // behind the data (see ld_after).
+        const StepWords sw = ld_after(st, tile_word + T);
+        const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
+        const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
+        const uint32_t start_mask = (sw.w0 & 1u) ? 0xFFu : 0u;
+        // words are non-decreasing, so (end < first) never holds; it keeps the tile-word
+        // loads above the branch with the decision
+        if (sw.skip | (end < first)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) keep_loaded<OPT>(G[u], W[u], M[u], V[u]);
+            return;
         }
-        wp[i] = w;
-        mp[i] = m;
-        hp[i] = Fmt<DT>::enc(w);
+        if (first == end) {
+            // one decay flag for the whole tile
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                update8<DT, OPT>(G[u], W[u], M[u], V[u], c, a, start_mask, h4, w4, m4, v4,
+                                 v0 + u * kFlatBlock + threadIdx.x);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t o = (uint32_t)(u * kFlatBlock + threadIdx.x) * kVec;
+                update8<DT, OPT>(G[u], W[u], M[u], V[u], c, a,
+                                 decay_bits(change, first, end, o, start_mask), h4, w4, m4, v4,
+                                 v0 + u * kFlatBlock + threadIdx.x);
+            }
+        }
+        return;
+    }
+
+    // the last tile, shorter than kFlatTile: guarded vectors, then the last n % 8
+    // elements on the scalar path
+    const StepWords sw = ld_after(st, tile_word + T);
+    if (sw.skip) return;
+    const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
+    const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
+    const uint32_t start_mask = (sw.w0 & 1u) ? 0xFFu : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t i = v0 + u * kFlatBlock + threadIdx.x;
+        if (i < nvec) {
+            uint4 G;
+            float4 W[2], M[2], V[2];
+            load8<OPT>(g4, w4, m4, v4, i, G, W, M, V);
+            const uint32_t o = (uint32_t)(u * kFlatBlock + threadIdx.x) * kVec;
+            update8<DT, OPT>(G, W, M, V, c, a, decay_bits(change, first, end, o, start_mask), h4,
+                             w4, m4, v4, i);
+        }
+    }
+    const uint64_t e = nvec * kVec + threadIdx.x;
+    if (e < s.n) {
+        const uint32_t o = (uint32_t)(e - (uint64_t)T * kFlatTile);
+        const bool decay = decay_bits(change, first, end, o, start_mask) & 1u;
+        update1<DT, OPT>(s.grad, s.half, s.master, s.m, s.v, e, c, a, decay);
     }
 }
 
@@ -527,6 +690,24 @@ static void launch_update_opt(int dtype, const Chunk* chunks, uint32_t nchunks, 
         update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kBlock, lds, stream>>>(chunks, nchunks, st, a);
     else
         update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kBlock, lds, stream>>>(chunks, nchunks, st, a);
+}
+
+template <int OPT>
+static void launch_flat_opt(int dtype, const FlatSpan& f, const DevState* st, const UpdateArgs& a,
+                            uint32_t lds, hipStream_t stream) {
+    if (dtype == 1)
+        flat_update_kernel<1, OPT><<<f.ntiles, kFlatBlock, lds, stream>>>(f, f.tile_word, f.change, st, a);
+    else
+        flat_update_kernel<2, OPT><<<f.ntiles, kFlatBlock, lds, stream>>>(f, f.tile_word, f.change, st, a);
+}
+
+hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const DevState* st,
+                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream) {
+    if (optimizer == 1)
+        launch_flat_opt<1>(dtype, f, st, a, lds_reserve, stream);
+    else
+        launch_flat_opt<0>(dtype, f, st, a, lds_reserve, stream);
+    return hipGetLastError();
 }
 
 // lds_reserve: dynamic LDS the kernel never touches, requested only to cap how many

@@ -47,6 +47,9 @@ def test_probe_rejects_bad_arguments():
         P.neox_probe_copy(0, 0, 16)
     with pytest.raises(RuntimeError):
         P.neox_probe_update_pattern(16, 16, 16, 16, 16, 7)
+    for shape in ((100, 2, 0), (256, 3, 0), (256, 2, -1), (256, 2, 17)):
+        with pytest.raises(RuntimeError):
+            P.neox_probe_update_pattern(16, 16, 16, 16, 16, 8, *shape)
 
 
 def test_default_config():
@@ -124,7 +127,7 @@ def _fake_seg(n=16, base=0x10000, flags=0):
     ("dp_world_size", 0), ("dtype", 3), ("scaler_mode", 2), ("growth_interval", 0),
     ("init_scale", 0.0), ("init_scale", 1e39), ("growth_factor", 0.5), ("backoff_factor", 0.0),
     ("backoff_factor", 1.5), ("min_scale", 0.0), ("init_step", -1), ("chunk_elems", 100),
-    ("chunk_elems", 257), ("chunk_elems", 1 << 25), ("optimizer", 2), ("segment_norms", 2)])
+    ("chunk_elems", 257), ("chunk_elems", 1 << 25), ("optimizer", 2), ("segment_norms", 2), ("chunked_update", 2)])
 def test_create_rejects_bad_config(field, value):
     cfg = Z.neox_zero1_default_config()
     setattr(cfg, field, value)
@@ -192,3 +195,4 @@ def test_null_handle_calls():
     assert L.neox_zero1_step_apply(None, None, C.c_float(1e-3), None) == Z.NEOX_EINVAL
     assert L.neox_scaler_set(None, None, None) == Z.NEOX_EINVAL
     assert L.neox_zero1_segment_sumsq(None, None, 0) == Z.NEOX_EINVAL
+    assert L.neox_zero1_update_path(None) == Z.NEOX_EINVAL

@@ -187,3 +187,77 @@ def test_resume_equals_continuous():
     oa, ob = _outputs(a), _outputs(b)
     for k in oa:
         assert torch.equal(oa[k], ob[k]), k
+
+
+def _path(w, shard, **over):
+    h = Z.neox_zero1_create(lib_config(w, **over), shard.neox_segments(),
+                            torch.cuda.current_stream().cuda_stream)
+    try:
+        return Z.neox_zero1_update_path(h)
+    finally:
+        Z.neox_zero1_destroy(h)
+
+
+def test_update_path_selection():
+    """The flat update runs exactly for a flat, 16-byte-aligned partition with the default
+    chunk size and chunked_update 0; every other layout takes the chunk table."""
+    w = _custom("paths", [5000, 3, 9000], [True, False, True])
+    flat = DeviceShard(w, flat=True)
+    assert _path(w, flat) == Z.NEOX_PATH_FLAT
+    assert _path(w, flat, chunked_update=1) == Z.NEOX_PATH_CHUNKED
+    assert _path(w, flat, chunk_elems=4096) == Z.NEOX_PATH_CHUNKED
+    assert _path(w, DeviceShard(w, flat=True, misalign=(0, 0, 1, 0, 0))) == Z.NEOX_PATH_CHUNKED
+    assert _path(w, DeviceShard(w, flat=False)) == Z.NEOX_PATH_CHUNKED
+    ws = _custom("paths_sgd", [5000, 3, 9000], [True, False, True], optimizer=1)
+    assert _path(ws, DeviceShard(ws, flat=True), optimizer=1) == Z.NEOX_PATH_FLAT
+
+
+# Segment lengths that put flag changes at 2,048- and 4,096-element boundaries, mid-tile,
+# inside one 8-element vector and several to a tile, over tens of full tiles and a
+# ragged last one with a scalar tail (55,499 elements).
+_MIXED_SIZES = [1, 4095, 4096, 7, 1, 9, 3000, 1096, 100, 100, 100, 8184, 5, 3, 17, 4096,
+                12_288, 2, 2, 2, 2, 2, 2, 2, 2, 8190, 6000, 2, 4093]
+_MIXED_DECAY = [i % 2 == 0 for i in range(len(_MIXED_SIZES))]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16], ids=["f16", "bf16"])
+def test_flat_mixed_decay_tiles(dtype):
+    """Flat update on tiles holding several segments with alternating decay flags, with an
+    overflow (skipped step) in a full tile: every element against the oracle."""
+    w = _custom("mixed_tiles", _MIXED_SIZES, _MIXED_DECAY, dtype, weight_decay=0.5)
+    w.injections = {2: [(20_000, "nan")]}
+    shard = DeviceShard(w, flat=True)
+    assert _path(w, shard) == Z.NEOX_PATH_FLAT
+    log(f"case flat mixed tiles dtype={dtype} n={w.numel}")
+    chk = run_sequence(w, 5, shard=shard, where=" flat mixed")
+    assert chk.ost.skipped_total == 1 and w.numel % 8 != 0 and w.numel > 13 * 4096
+
+
+@pytest.mark.parametrize("optimizer", [0, 1], ids=["adamw", "sgd"])
+def test_flat_equals_chunked_bitwise(optimizer):
+    """Both update kernels run the same arithmetic, so on the same inputs they agree bit
+    for bit: master, m, v, half and the scaler state, over clean and skipped steps."""
+    w = _custom("flat_vs_chunked", _MIXED_SIZES * 3, _MIXED_DECAY * 3, optimizer=optimizer,
+                weight_decay=0.5)
+    w.injections = {1: [(70_000, "+inf")], 3: [(w.numel - 1, "-inf")]}
+    stream = torch.cuda.current_stream().cuda_stream
+    outs, states = [], []
+    for chunked in (0, 1):
+        shard = DeviceShard(w, flat=True)
+        shard.init_()
+        h = Z.neox_zero1_create(lib_config(w, chunked_update=chunked, optimizer=optimizer),
+                                shard.neox_segments(), stream)
+        assert Z.neox_zero1_update_path(h) == (Z.NEOX_PATH_CHUNKED if chunked else Z.NEOX_PATH_FLAT)
+        log(f"case flat vs chunked optimizer={optimizer} chunked={chunked}")
+        for k in range(6):
+            shard.grads_(k, Z.neox_scaler_state(h).loss_scale)
+            Z.neox_zero1_step(h, 1e-3, stream)
+        st = Z.neox_scaler_state(h)
+        states.append((st.loss_scale, st.step, st.skipped_total, st.good_steps, st.last_sumsq))
+        Z.neox_zero1_destroy(h)
+        torch.cuda.synchronize()
+        outs.append({k: torch.cat([s[k].reshape(-1) for s in shard.segs]).clone()
+                     for k in (("half", "master", "m") if optimizer else ("half", "master", "m", "v"))})
+    assert states[0] == states[1] and states[0][2] == 2
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
