@@ -191,10 +191,9 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
 /* Enqueue one step on hip_stream and return without waiting: a norm/overflow pass
  * over every gradient, a one-block finalize (skip decision, clip coefficient, step
  * count, bias corrections, loss-scale update, all on the device), and the fused
- * unscale + clip + AdamW + cast update, which writes nothing when the finalize decided
- * to skip (the chunked update then returns at once; the flat one has already issued
- * its tile's loads and drops them).  The gradient must be complete in stream order
- * before this call.
+ * unscale + clip + AdamW + cast update, which returns before loading its data when the
+ * finalize decided to skip.  The gradient must be complete in stream order before this
+ * call.
  * On a skipped step master, exp_avg, exp_avg_sq and half are not written.
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
 int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream);

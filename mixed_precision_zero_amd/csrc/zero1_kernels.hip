@@ -89,11 +89,22 @@ struct Fmt<2> {
 #ifndef NZ1_UPDATE_NT_STORE
 #define NZ1_UPDATE_NT_STORE 0
 #endif
+#ifndef NZ1_UPDATE_BLOCK
+#define NZ1_UPDATE_BLOCK 256
+#endif
+constexpr int kUpdateBlock = NZ1_UPDATE_BLOCK;   // threads per block of the chunked update
 #ifndef NZ1_UPDATE_UNROLL
 #define NZ1_UPDATE_UNROLL 2
 #endif
 #ifndef NZ1_UPDATE_REVERSE
 #define NZ1_UPDATE_REVERSE 1
+#endif
+// 1: the flat update issues its tile's loads before it knows the finalize's decision (a
+// skipped step then reads the tile and drops it).  0: it waits for the decision first.
+// At 2 blocks per CU the other block hides that wait and the two measure the same, so
+// the default keeps skipped steps cheap.
+#ifndef NZ1_FLAT_SPECULATE
+#define NZ1_FLAT_SPECULATE 0
 #endif
 #ifndef NZ1_UPDATE_FAST_DIV
 #define NZ1_UPDATE_FAST_DIV 0
@@ -450,7 +461,7 @@ __device__ __forceinline__ void load8(const uint4* __restrict__ g4, const float4
 
 // Generic layout: one block per entry of the chunk table.
 template <int DT, int U, int OPT>
-__global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict__ chunks,
+__global__ __launch_bounds__(kUpdateBlock) void update_kernel(const Chunk* __restrict__ chunks,
                                                         uint32_t nchunks,
                                                         const DevState* __restrict__ st,
                                                         UpdateArgs a) {
@@ -484,24 +495,24 @@ __global__ __launch_bounds__(kBlock) void update_kernel(const Chunk* __restrict_
         float4* __restrict__ m4 = reinterpret_cast<float4*>(mp);
         float4* __restrict__ v4 = reinterpret_cast<float4*>(vp);
         const uint32_t nvec = len / kVec;
-        for (uint32_t base = 0; base < nvec; base += U * kBlock) {
+        for (uint32_t base = 0; base < nvec; base += U * kUpdateBlock) {
             uint4 G[U];
             float4 W[U][2], M[U][2], V[U][2];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t i = base + u * kBlock + threadIdx.x;
+                const uint32_t i = base + u * kUpdateBlock + threadIdx.x;
                 if (i < nvec) load8<OPT>(g4, w4, m4, v4, i, G[u], W[u], M[u], V[u]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t i = base + u * kBlock + threadIdx.x;
+                const uint32_t i = base + u * kUpdateBlock + threadIdx.x;
                 if (i < nvec) update8<DT, OPT>(G[u], W[u], M[u], V[u], c, a, dmask, h4, w4, m4, v4, i);
             }
         }
         done = nvec * kVec;
     }
     // scalar path: chunks that are not 16-byte aligned, and the last < 8 elements
-    for (uint32_t i = done + threadIdx.x; i < len; i += kBlock)
+    for (uint32_t i = done + threadIdx.x; i < len; i += kUpdateBlock)
         update1<DT, OPT>(gp, hp, wp, mp, vp, i, c, a, (flags & CH_DECAY) != 0);
 }
 
@@ -519,9 +530,10 @@ __device__ __forceinline__ uint32_t decay_bits(const uint32_t* __restrict__ chan
     return mask;
 }
 
-// Uses loaded values (register operands of an empty asm).  Placed on the skip branch,
-// it gives the loads a user on both sides of that branch, so the compiler cannot sink
-// them below it: they stay in flight while the block waits for the decision.
+// Uses loaded values (register operands of an empty asm).  Placed on the skip branch
+// after the loads, it gives them a user on both sides of that branch, so the compiler
+// cannot sink them below it (with NZ1_FLAT_SPECULATE they are in flight while the block
+// waits for the decision).
 template <int OPT>
 __device__ __forceinline__ void keep_loaded(const uint4& G, const float4 (&W)[2],
                                             const float4 (&M)[2], const float4 (&V)[2]) {
@@ -533,7 +545,7 @@ __device__ __forceinline__ void keep_loaded(const uint4& G, const float4 (&W)[2]
 // coefficients, and its tile's two decay words.  Read with relaxed atomic loads: those
 // are vector-memory loads, which return in issue order, and the compiler keeps them in
 // program order after the data loads, so the block issues its whole tile before it
-// waits for anything.  (Plain loads of these uniform values would become scalar loads,
+// waits for them.  (Plain loads of these uniform values would become scalar loads,
 // whose out-of-order completion makes the compiler wait for all of them before the data
 // loads go out.)  Workgroup scope suffices: the values were written by an earlier
 // kernel, complete before this one started.
@@ -558,10 +570,10 @@ __device__ __forceinline__ StepWords ld_after(const DevState* st, const uint32_t
 }
 
 // Flat layout: the segments tile five contiguous 16-byte-aligned arrays (a flat
-// partition), so tile T's addresses follow from T alone.  A block issues its data loads
-// together with the fetch of its tile's decay words and of the finalize's decision,
-// instead of waiting for a work descriptor before its first data load.  On a skipped
-// step the tile is read and dropped; nothing is written.
+// partition), so tile T's addresses follow from T alone: a block needs no work
+// descriptor (a per-block load that streaming has evicted to HBM) before its first data
+// load, only the finalize's decision, which every block reads and the L2 keeps.  The
+// tile's decay words and the coefficients are fetched behind the data.
 template <int DT, int OPT>
 __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
                                                              const uint32_t* __restrict__ tile_word,
@@ -578,6 +590,14 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
     float4* __restrict__ m4 = reinterpret_cast<float4*>(s.m);
     float4* __restrict__ v4 = reinterpret_cast<float4*>(s.v);
 
+#if !NZ1_FLAT_SPECULATE
+    // Wait for the decision before loading: a skipped step then reads nothing here.  The
+    // base pointers are 16-byte aligned, so their low-bit term never fires; it makes the
+    // branch wait for them too, so they are fetched with the state pointer, not after.
+    const uintptr_t low = ((uintptr_t)s.grad | (uintptr_t)s.half | (uintptr_t)s.master |
+                           (uintptr_t)s.m | (uintptr_t)s.v) & 1u;
+    if (st->skip | (int32_t)low) return;
+#endif
     if (T + 1 < s.ntiles || s.n % kFlatTile == 0) {
         // a full tile: every thread owns U whole vectors
         uint4 G[U];
@@ -687,9 +707,9 @@ template <int OPT>
 static void launch_update_opt(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
                               const UpdateArgs& a, uint32_t lds, hipStream_t stream) {
     if (dtype == 1)
-        update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kBlock, lds, stream>>>(chunks, nchunks, st, a);
+        update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kUpdateBlock, lds, stream>>>(chunks, nchunks, st, a);
     else
-        update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kBlock, lds, stream>>>(chunks, nchunks, st, a);
+        update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kUpdateBlock, lds, stream>>>(chunks, nchunks, st, a);
 }
 
 template <int OPT>
