@@ -10,8 +10,10 @@
 //   finalize  one block; fixed-order sum of the per-block partials, then the skip
 //             decision, clip coefficient, step count, bias corrections and the loss
 //             scale update, written to the device state block.
-//   update    one block per chunk; returns at once on a skipped step, otherwise
-//             unscale + clip + AdamW + cast with 16-byte loads and stores.
+//   update    returns at once on a skipped step, otherwise unscale + clip + AdamW +
+//             cast with 16-byte loads and stores: flat_update_kernel (one block per
+//             2,048-element tile of a flat partition, addresses from the block index)
+//             or update_kernel (one block per entry of the chunk table, any layout).
 // Sources: FP32 Adam state with FP16 weights and dynamic loss scaling [OPT: Open
 // Pre-trained Transformer Language Models, paper card, 计算设置]; pre-divide factor
 // and clipping at 1.0 / 0.3 [same card, 方法适配]; each rank updates only its shard
@@ -459,34 +461,13 @@ __device__ __forceinline__ void load8(const uint4* __restrict__ g4, const float4
     }
 }
 
-// Generic layout: one block per entry of the chunk table.
+// The update of one chunk whose descriptor fields are in registers.
 template <int DT, int U, int OPT>
-__global__ __launch_bounds__(kUpdateBlock) void update_kernel(const Chunk* __restrict__ chunks,
-                                                        uint32_t nchunks,
-                                                        const DevState* __restrict__ st,
-                                                        UpdateArgs a) {
-    // NZ1_UPDATE_REVERSE walks the chunks last-to-first, so the first gradients the
-    // update reads are the ones the norm pass read last.
-    const Chunk* ch = chunks + (NZ1_UPDATE_REVERSE ? nchunks - 1 - blockIdx.x : blockIdx.x);
-    // The descriptor and the finalize's decision are fetched together: the early exit
-    // below tests both, so neither load waits for the other.
-    const uint32_t len = ch->len;
-    const uint32_t flags = ch->flags;
-    const uint16_t* __restrict__ gp = ch->grad;
-    uint16_t* __restrict__ hp = ch->half;
-    float* __restrict__ wp = ch->master;
-    float* __restrict__ mp = ch->m;
-    float* __restrict__ vp = ch->v;
-    const int32_t skip = st->skip;
-    const Coefs c{st->gscale, st->rbc1, st->rsbc2};
-    // Chunks are never empty, their pointers are at least 2-byte aligned and flags use
-    // the low bits only, so the last two terms never fire; they make the branch wait for
-    // the whole descriptor at once.
-    const uint32_t odd = (uint32_t)(((uintptr_t)gp | (uintptr_t)hp | (uintptr_t)wp |
-                                     (uintptr_t)mp | (uintptr_t)vp) & 1u) | (flags >> 31);
-    if (skip | (len == 0) | odd) return;
+__device__ __forceinline__ void run_chunk(const uint16_t* __restrict__ gp, uint16_t* __restrict__ hp,
+                                          float* __restrict__ wp, float* __restrict__ mp,
+                                          float* __restrict__ vp, uint32_t len, uint32_t flags,
+                                          const Coefs& c, const UpdateArgs& a) {
     const uint32_t dmask = (flags & CH_DECAY) ? 0xFFu : 0u;
-
     uint32_t done = 0;
     if (flags & CH_VEC) {
         const uint4* __restrict__ g4 = reinterpret_cast<const uint4*>(gp);
@@ -514,6 +495,39 @@ __global__ __launch_bounds__(kUpdateBlock) void update_kernel(const Chunk* __res
     // scalar path: chunks that are not 16-byte aligned, and the last < 8 elements
     for (uint32_t i = done + threadIdx.x; i < len; i += kUpdateBlock)
         update1<DT, OPT>(gp, hp, wp, mp, vp, i, c, a, (flags & CH_DECAY) != 0);
+}
+
+// NZ1_UPDATE_REVERSE walks the chunks last-to-first, so the first gradients the update
+// reads are the ones the norm pass read last.
+__device__ __forceinline__ const Chunk* chunk_at(const Chunk* chunks, uint32_t nchunks, uint32_t k) {
+    return chunks + (NZ1_UPDATE_REVERSE ? nchunks - 1 - k : k);
+}
+
+// Generic layout: one block per entry of the chunk table.
+template <int DT, int U, int OPT>
+__global__ __launch_bounds__(kUpdateBlock) void update_kernel(const Chunk* __restrict__ chunks,
+                                                              uint32_t nchunks,
+                                                              const DevState* __restrict__ st,
+                                                              UpdateArgs a) {
+    const Chunk* ch = chunk_at(chunks, nchunks, blockIdx.x);
+    // The descriptor and the finalize's decision are fetched together: the early exit
+    // below tests both, so neither load waits for the other.
+    const uint32_t len = ch->len;
+    const uint32_t flags = ch->flags;
+    const uint16_t* __restrict__ gp = ch->grad;
+    uint16_t* __restrict__ hp = ch->half;
+    float* __restrict__ wp = ch->master;
+    float* __restrict__ mp = ch->m;
+    float* __restrict__ vp = ch->v;
+    const int32_t skip = st->skip;
+    const Coefs c{st->gscale, st->rbc1, st->rsbc2};
+    // Chunks are never empty, their pointers are at least 2-byte aligned and flags use
+    // the low bits only, so the last two terms never fire; they make the branch wait for
+    // the whole descriptor at once.
+    const uint32_t odd = (uint32_t)(((uintptr_t)gp | (uintptr_t)hp | (uintptr_t)wp |
+                                     (uintptr_t)mp | (uintptr_t)vp) & 1u) | (flags >> 31);
+    if (skip | (len == 0) | odd) return;
+    run_chunk<DT, U, OPT>(gp, hp, wp, mp, vp, len, flags, c, a);
 }
 
 // Decay bits of the n <= 8 consecutive elements starting at offset o of a tile: the
