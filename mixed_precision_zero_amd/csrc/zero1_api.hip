@@ -34,10 +34,10 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Work-unit sizes (elements), measured best on MI355X: the update wants small blocks
-// (one 16-byte vector per array per thread and pass), the read-only norm pass wants
-// more bytes per block.
+// (2,048 elements: 128 threads x two 16-byte vectors per array) at low occupancy, the
+// read-only norm pass wants more bytes per block at full occupancy.
 #ifndef NZ1_UPDATE_CHUNK
-#define NZ1_UPDATE_CHUNK 4096
+#define NZ1_UPDATE_CHUNK 2048
 #endif
 #ifndef NZ1_NORM_CHUNK
 #define NZ1_NORM_CHUNK 16384
@@ -45,7 +45,7 @@ int hip_fail(hipError_t e, const char* what) {
 // Blocks per CU for each pass (0 = as many as registers allow).  The cap is enforced by
 // reserving an equal share of the CU's LDS per block.
 #ifndef NZ1_UPDATE_BLOCKS_PER_CU
-#define NZ1_UPDATE_BLOCKS_PER_CU 0
+#define NZ1_UPDATE_BLOCKS_PER_CU 2
 #endif
 #ifndef NZ1_NORM_BLOCKS_PER_CU
 #define NZ1_NORM_BLOCKS_PER_CU 0
