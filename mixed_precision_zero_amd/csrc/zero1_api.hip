@@ -34,13 +34,14 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Work-unit sizes (elements), measured best on MI355X: the update wants small blocks
-// (2,048 elements: 128 threads x two 16-byte vectors per array) at low occupancy, the
-// read-only norm pass wants more bytes per block at full occupancy.
+// (2,048 elements: 128 threads x two 16-byte vectors per array) at 2 blocks per CU, the
+// read-only norm pass more bytes per block (32K elements, 8 loads in flight per thread)
+// at 4 blocks per CU.
 #ifndef NZ1_UPDATE_CHUNK
 #define NZ1_UPDATE_CHUNK 2048
 #endif
 #ifndef NZ1_NORM_CHUNK
-#define NZ1_NORM_CHUNK 16384
+#define NZ1_NORM_CHUNK 32768
 #endif
 // Blocks per CU for each pass (0 = as many as registers allow).  The cap is enforced by
 // reserving an equal share of the CU's LDS per block.
@@ -48,7 +49,7 @@ int hip_fail(hipError_t e, const char* what) {
 #define NZ1_UPDATE_BLOCKS_PER_CU 2
 #endif
 #ifndef NZ1_NORM_BLOCKS_PER_CU
-#define NZ1_NORM_BLOCKS_PER_CU 0
+#define NZ1_NORM_BLOCKS_PER_CU 4
 #endif
 #ifndef NZ1_FLAT_BLOCKS_PER_CU
 #define NZ1_FLAT_BLOCKS_PER_CU 2

@@ -85,6 +85,10 @@ struct Fmt<2> {
 #ifndef NZ1_NORM_NT_LOAD
 #define NZ1_NORM_NT_LOAD 1
 #endif
+#ifndef NZ1_NORM_UNROLL
+#define NZ1_NORM_UNROLL 8
+#endif
+constexpr int kNormUnroll = NZ1_NORM_UNROLL;   // 16-byte loads in flight per norm thread
 #ifndef NZ1_UPDATE_NT_LOAD
 #define NZ1_UPDATE_NT_LOAD 0
 #endif
@@ -208,15 +212,13 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ 
             const uint4* __restrict__ g4 = reinterpret_cast<const uint4*>(g);
             const uint32_t nvec = len / kVec;
             uint32_t i = threadIdx.x;
-            for (; i + 3 * kBlock < nvec; i += 4 * kBlock) {
-                const uint4 q0 = ld16<NZ1_NORM_NT_LOAD>(g4 + i);
-                const uint4 q1 = ld16<NZ1_NORM_NT_LOAD>(g4 + i + kBlock);
-                const uint4 q2 = ld16<NZ1_NORM_NT_LOAD>(g4 + i + 2 * kBlock);
-                const uint4 q3 = ld16<NZ1_NORM_NT_LOAD>(g4 + i + 3 * kBlock);
-                sq8<DT>(q0, inv, a0, a1);
-                sq8<DT>(q1, inv, a0, a1);
-                sq8<DT>(q2, inv, a0, a1);
-                sq8<DT>(q3, inv, a0, a1);
+            // kNormUnroll loads in flight per thread, then their sums in order
+            for (; i + (kNormUnroll - 1) * kBlock < nvec; i += kNormUnroll * kBlock) {
+                uint4 q[kNormUnroll];
+#pragma unroll
+                for (int u = 0; u < kNormUnroll; ++u) q[u] = ld16<NZ1_NORM_NT_LOAD>(g4 + i + u * kBlock);
+#pragma unroll
+                for (int u = 0; u < kNormUnroll; ++u) sq8<DT>(q[u], inv, a0, a1);
             }
             for (; i < nvec; i += kBlock) sq8<DT>(ld16<NZ1_NORM_NT_LOAD>(g4 + i), inv, a0, a1);
             done = nvec * kVec;
