@@ -58,6 +58,9 @@ extern "C" {
 #define NEOX_PATH_CHUNKED 0     /* update driven by the per-chunk work table    */
 #define NEOX_PATH_FLAT    1     /* update addresses a flat partition's tiles    */
 
+#define NEOX_CHUNK_DECAY 1u     /* chunk's elements receive decoupled decay     */
+#define NEOX_CHUNK_VEC   2u     /* all five arrays 16-byte aligned at its start */
+
 #define NEOX_SEG_DECAY 1u       /* segment receives decoupled weight decay      */
 #define NEOX_PAD_TENSOR 0xFFFFFFFFu
 
@@ -252,6 +255,47 @@ int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);
 /* Which update kernel the handle runs: NEOX_PATH_FLAT or NEOX_PATH_CHUNKED (see
  * chunked_update).  Errors: NEOX_EINVAL (null handle). */
 int neox_zero1_update_path(const neox_zero1* h);
+
+/* The work decomposition neox_zero1_create() builds for a segment list — the segment /
+ * chunk bookkeeping of the multi-tensor step [NeoX, 技术深度解析: each rank updates the
+ * shard it owns, held as a list of tensor pieces] — computed on the host with the same
+ * validation and no device call, for inspection and tests.  Chunks never straddle a
+ * segment: a segment whose five arrays become 16-byte aligned after h < 8 elements
+ * starts with an h-element chunk without NEOX_CHUNK_VEC, then takes chunks of
+ * chunk_elems (the last one shorter), all with NEOX_CHUNK_VEC; a segment whose arrays
+ * can never be aligned together gets chunks without it.  Chunks are listed in segment
+ * order.  On the flat path tile_words[flat_tiles + 1] and changes[flat_changes] hold the
+ * tile table: word T = (index in changes of tile T's first decay-flag change) << 1 |
+ * decay flag of the tile's first element; changes holds in-tile offsets where the flag
+ * flips; word flat_tiles closes the last list. */
+typedef struct neox_chunk_info {
+    uint64_t offset;               /* first element of the chunk within its segment      */
+    uint32_t seg;                  /* index in segs                                      */
+    uint32_t len;                  /* elements, 1 .. chunk_elems                         */
+    uint32_t flags;                /* NEOX_CHUNK_DECAY | NEOX_CHUNK_VEC                  */
+    uint32_t reserved;             /* 0                                                  */
+} neox_chunk_info;
+
+typedef struct neox_zero1_plan_t {
+    uint64_t numel;                /* elements over all segments                        */
+    uint64_t update_chunks;        /* entries of the update chunk table                 */
+    uint64_t norm_chunks;          /* entries of the norm pass's table                  */
+    uint64_t flat_tiles;           /* tiles of the flat update; 0 on the chunked path   */
+    uint64_t flat_changes;         /* in-tile decay-flag changes (flat path)            */
+    uint32_t chunk_elems;          /* update chunk length                               */
+    uint32_t norm_chunk_elems;     /* norm chunk length                                 */
+    uint32_t tile_elems;           /* flat tile length                                  */
+    int32_t  update_path;          /* NEOX_PATH_FLAT or NEOX_PATH_CHUNKED               */
+} neox_zero1_plan_t;
+
+/* Fills *out (host) and the first min(cap, size) entries of each host table; a table
+ * may be NULL with capacity 0.  The segments' pointers are only compared, never
+ * dereferenced.  Errors: as neox_zero1_create's validation (NEOX_EINVAL), NEOX_EINVAL
+ * for a NULL out or a NULL table with nonzero capacity, NEOX_ENOMEM. */
+int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg,
+                    neox_zero1_plan_t* out, neox_chunk_info* chunks, uint64_t chunk_cap,
+                    uint32_t* tile_words, uint64_t word_cap, uint32_t* changes,
+                    uint64_t change_cap);
 
 /* Text of the last error raised on the calling thread (never NULL). */
 const char* neox_zero1_last_error(void);

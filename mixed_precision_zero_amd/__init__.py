@@ -20,6 +20,7 @@ NEOX_F16, NEOX_BF16 = 1, 2
 NEOX_SCALER_DYNAMIC, NEOX_SCALER_STATIC = 0, 1
 NEOX_OPT_ADAMW, NEOX_OPT_SGD = 0, 1
 NEOX_PATH_CHUNKED, NEOX_PATH_FLAT = 0, 1
+NEOX_CHUNK_DECAY, NEOX_CHUNK_VEC = 1, 2
 NEOX_SEG_DECAY = 1
 NEOX_PAD_TENSOR = 0xFFFFFFFF
 
@@ -58,6 +59,18 @@ class neox_scaler_state_t(C.Structure):
                 ("device_loss_scale", C.c_void_p)]
 
 
+class neox_chunk_info(C.Structure):
+    _fields_ = [("offset", C.c_uint64), ("seg", C.c_uint32), ("len", C.c_uint32),
+                ("flags", C.c_uint32), ("reserved", C.c_uint32)]
+
+
+class neox_zero1_plan_t(C.Structure):
+    _fields_ = [("numel", C.c_uint64), ("update_chunks", C.c_uint64), ("norm_chunks", C.c_uint64),
+                ("flat_tiles", C.c_uint64), ("flat_changes", C.c_uint64),
+                ("chunk_elems", C.c_uint32), ("norm_chunk_elems", C.c_uint32),
+                ("tile_elems", C.c_uint32), ("update_path", C.c_int32)]
+
+
 class neox_shard_segment(C.Structure):
     _fields_ = [("shard_offset", C.c_uint64), ("numel", C.c_uint64),
                 ("tensor_offset", C.c_uint64), ("tensor_id", C.c_uint32), ("flags", C.c_uint32)]
@@ -69,7 +82,7 @@ EXPORTS = ("neox_zero1_default_config", "neox_zero1_partition", "neox_zero1_crea
            "neox_zero1_step_local", "neox_zero1_step_apply", "neox_scaler_set",
            "neox_zero1_segment_sumsq",
            "neox_zero1_timing_begin", "neox_zero1_timing_end", "neox_zero1_update_path",
-           "neox_zero1_last_error")
+           "neox_zero1_plan", "neox_zero1_last_error")
 
 _lib = None
 
@@ -99,6 +112,9 @@ def lib():
         L.neox_zero1_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
         L.neox_zero1_timing_end.argtypes = [C.c_void_p, P(C.c_double), P(C.c_int64)]
         L.neox_zero1_update_path.argtypes = [C.c_void_p]
+        L.neox_zero1_plan.argtypes = [P(neox_zero1_config), P(neox_segment), C.c_uint64,
+                                      P(neox_zero1_plan_t), P(neox_chunk_info), C.c_uint64,
+                                      P(C.c_uint32), C.c_uint64, P(C.c_uint32), C.c_uint64]
         L.neox_zero1_last_error.argtypes = []
         L.neox_zero1_last_error.restype = C.c_char_p
         for name in EXPORTS:
@@ -208,6 +224,24 @@ def neox_zero1_update_path(h: int) -> int:
     if rc < 0:
         _check(rc)
     return rc
+
+
+def neox_zero1_plan(cfg: neox_zero1_config, segs, tables: bool = True):
+    """-> (neox_zero1_plan_t, chunk list, tile words, changes): the decomposition create()
+    would build, computed on the host (no device call; pointers are only compared)."""
+    arr = (neox_segment * max(1, len(segs)))(*segs)
+    plan = neox_zero1_plan_t()
+    _check(lib().neox_zero1_plan(C.byref(cfg), arr, len(segs), C.byref(plan), None, 0, None, 0,
+                                 None, 0))
+    if not tables:
+        return plan, [], [], []
+    chunks = (neox_chunk_info * max(1, plan.update_chunks))()
+    nw = plan.flat_tiles + 1 if plan.update_path == NEOX_PATH_FLAT else 0
+    words = (C.c_uint32 * max(1, nw))()
+    changes = (C.c_uint32 * max(1, plan.flat_changes))()
+    _check(lib().neox_zero1_plan(C.byref(cfg), arr, len(segs), C.byref(plan), chunks,
+                                 plan.update_chunks, words, nw, changes, plan.flat_changes))
+    return plan, list(chunks[:plan.update_chunks]), list(words[:nw]), list(changes[:plan.flat_changes])
 
 
 def neox_zero1_timing_end(h: int):

@@ -360,44 +360,106 @@ static void free_handle(neox_zero1* h) {
     delete h;
 }
 
-extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs,
-                                 uint64_t nseg, void* hip_stream, neox_zero1** out) {
-    if (!out) return fail(NEOX_EINVAL, "out is NULL");
-    *out = nullptr;
+// The work decomposition of a segment list: what create() uploads and neox_zero1_plan()
+// describes.  Validates the config and the segments first.
+struct Plan {
+    uint32_t C = 0;                        // update chunk length
+    uint32_t C1 = 0;                       // norm chunk length
+    std::vector<Chunk> table, norm_table;  // update and norm work tables
+    bool flat = false;                     // flat partition: the update runs over tiles
+    uint64_t numel = 0;
+    std::vector<uint32_t> tile_word, change;
+};
+
+static int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg,
+                     Plan& p) {
     if (!cfg) return fail(NEOX_EINVAL, "cfg is NULL");
     int rc = validate_config(cfg);
     if (rc) return rc;
     rc = validate_segments(segs, nseg, cfg->optimizer == NEOX_OPT_ADAMW);
     if (rc) return rc;
+    if (cfg->segment_norms && nseg >= (1u << 24))
+        return fail(NEOX_EINVAL, "segment_norms supports fewer than 2^24 segments");
 
     // update chunks of C elements; norm chunks of the smallest multiple of C that is
     // at least kNormChunk
-    const uint32_t C = cfg->chunk_elems ? cfg->chunk_elems : kDefaultChunk;
-    const uint64_t C1_64 = C >= kNormChunk ? C : (uint64_t)(kNormChunk + C - 1) / C * C;
-    const uint32_t C1 = C1_64 > (1u << 24) ? C : (uint32_t)C1_64;
-    std::vector<Chunk> table, norm_table;
+    p.C = cfg->chunk_elems ? cfg->chunk_elems : kDefaultChunk;
+    const uint64_t C1_64 = p.C >= kNormChunk ? p.C : (uint64_t)(kNormChunk + p.C - 1) / p.C * p.C;
+    p.C1 = C1_64 > (1u << 24) ? p.C : (uint32_t)C1_64;
+    for (uint64_t k = 0; k < nseg; ++k) p.numel += segs[k].numel;
     try {
-        build_chunks(segs, nseg, C, table);
-        build_chunks(segs, nseg, C1, norm_table);
+        build_chunks(segs, nseg, p.C, p.table);
+        build_chunks(segs, nseg, p.C1, p.norm_table);
     } catch (const std::bad_alloc&) {
         return fail(NEOX_ENOMEM, "host allocation of the chunk table");
     }
-    if (table.size() >= (1ull << 24)) return fail(NEOX_EINVAL, "%zu chunks: raise chunk_elems", table.size());
+    // one block per chunk; the grid's x size in work-items is 32-bit
+    if (p.table.size() >= (1ull << 24)) return fail(NEOX_EINVAL, "%zu chunks: raise chunk_elems", p.table.size());
 
     const bool has_v = cfg->optimizer == NEOX_OPT_ADAMW;
     uint64_t flat_n = 0;
-    const bool flat = !cfg->chunked_update && cfg->chunk_elems == 0 &&
-                      flat_layout(segs, nseg, has_v, &flat_n) &&
-                      // the grid's x size in work-items is 32-bit
-                      (flat_n + kFlatTile - 1) / kFlatTile * kFlatBlock < (1ull << 32);
-    std::vector<uint32_t> tile_word, change;
-    if (flat) {
+    p.flat = !cfg->chunked_update && cfg->chunk_elems == 0 &&
+             flat_layout(segs, nseg, has_v, &flat_n) &&
+             (flat_n + kFlatTile - 1) / kFlatTile * kFlatBlock < (1ull << 32);
+    if (p.flat) {
         try {
-            build_flat_tables(segs, nseg, flat_n, tile_word, change);
+            build_flat_tables(segs, nseg, flat_n, p.tile_word, p.change);
         } catch (const std::bad_alloc&) {
             return fail(NEOX_ENOMEM, "host allocation of the tile table");
         }
     }
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg,
+                               neox_zero1_plan_t* out, neox_chunk_info* chunks, uint64_t chunk_cap,
+                               uint32_t* tile_words, uint64_t word_cap, uint32_t* changes,
+                               uint64_t change_cap) {
+    if (!out) return fail(NEOX_EINVAL, "out is NULL");
+    if ((chunk_cap && !chunks) || (word_cap && !tile_words) || (change_cap && !changes))
+        return fail(NEOX_EINVAL, "NULL table with a nonzero capacity");
+    Plan p;
+    const int rc = make_plan(cfg, segs, nseg, p);
+    if (rc) return rc;
+    std::memset(out, 0, sizeof *out);
+    out->numel = p.numel;
+    out->update_chunks = p.table.size();
+    out->norm_chunks = p.norm_table.size();
+    out->flat_tiles = p.flat ? p.tile_word.size() - 1 : 0;
+    out->flat_changes = p.change.size();
+    out->chunk_elems = p.C;
+    out->norm_chunk_elems = p.C1;
+    out->tile_elems = kFlatTile;
+    out->update_path = p.flat ? NEOX_PATH_FLAT : NEOX_PATH_CHUNKED;
+    for (uint64_t i = 0; i < chunk_cap && i < p.table.size(); ++i) {
+        const Chunk& c = p.table[i];
+        const neox_segment& sg = segs[c.seg];
+        chunks[i].offset = (uint64_t)(c.master - sg.master);
+        chunks[i].seg = c.seg;
+        chunks[i].len = c.len;
+        chunks[i].flags = ((c.flags & CH_DECAY) ? NEOX_CHUNK_DECAY : 0u) |
+                          ((c.flags & CH_VEC) ? NEOX_CHUNK_VEC : 0u);
+        chunks[i].reserved = 0;
+    }
+    for (uint64_t i = 0; i < word_cap && i < p.tile_word.size(); ++i) tile_words[i] = p.tile_word[i];
+    for (uint64_t i = 0; i < change_cap && i < p.change.size(); ++i) changes[i] = p.change[i];
+    return NEOX_OK;
+}
+
+extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs,
+                                 uint64_t nseg, void* hip_stream, neox_zero1** out) {
+    if (!out) return fail(NEOX_EINVAL, "out is NULL");
+    *out = nullptr;
+    Plan plan;
+    const int rc = make_plan(cfg, segs, nseg, plan);
+    if (rc) return rc;
+    std::vector<Chunk>& table = plan.table;
+    std::vector<Chunk>& norm_table = plan.norm_table;
+    std::vector<uint32_t>& tile_word = plan.tile_word;
+    std::vector<uint32_t>& change = plan.change;
+    const bool flat = plan.flat;
+    const bool has_v = cfg->optimizer == NEOX_OPT_ADAMW;
+    const uint64_t flat_n = plan.numel;
 
     neox_zero1* h = new (std::nothrow) neox_zero1();
     if (!h) return fail(NEOX_ENOMEM, "host allocation of the handle");
@@ -426,10 +488,6 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
     h->nseg = (uint32_t)nseg;
     std::vector<uint32_t> seg_range;
-    if (cfg->segment_norms && nseg >= (1u << 24)) {
-        free_handle(h);
-        return fail(NEOX_EINVAL, "segment_norms supports fewer than 2^24 segments");
-    }
     if (cfg->segment_norms) {
         // norm chunks are built segment by segment, so each segment owns a contiguous range
         seg_range.assign(2 * nseg, 0);
