@@ -498,7 +498,8 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
         }
     }
 
-    e = hipMalloc(&h->d_chunks, table.size() * sizeof(Chunk));
+    // the update chunk table is uploaded only when the chunked update runs
+    e = flat ? hipSuccess : hipMalloc(&h->d_chunks, table.size() * sizeof(Chunk));
     if (e == hipSuccess) e = hipMalloc(&h->d_norm_chunks, norm_table.size() * sizeof(Chunk));
     if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_range, seg_range.size() * sizeof(uint32_t));
     if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_sumsq, nseg * sizeof(double));
@@ -525,7 +526,8 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     st.inv = unscale_factor(cfg->predivide_factor, (double)cfg->dp_world_size, st.loss_scale);
     st.skip = 1;
 
-    e = hipMemcpyAsync(h->d_chunks, table.data(), table.size() * sizeof(Chunk), hipMemcpyHostToDevice, stream);
+    if (!flat)
+        e = hipMemcpyAsync(h->d_chunks, table.data(), table.size() * sizeof(Chunk), hipMemcpyHostToDevice, stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(h->d_norm_chunks, norm_table.data(), norm_table.size() * sizeof(Chunk),
                            hipMemcpyHostToDevice, stream);
