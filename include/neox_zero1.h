@@ -31,6 +31,9 @@
  *     across the ABI.  Arguments are validated before any work is enqueued; on error
  *     nothing is enqueued and neox_zero1_last_error() describes the failure.
  *   - A handle may be used by one host thread at a time.
+ *   - A handle belongs to the device current at neox_zero1_create(); every segment array
+ *     must live on it, and later calls must pass a stream of that device (or NULL with
+ *     that device current).
  */
 #ifndef NEOX_ZERO1_H
 #define NEOX_ZERO1_H
