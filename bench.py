@@ -196,9 +196,10 @@ def copy_probe(nbytes):
     print(f"[bench] copy probe: 3 x {nbytes} bytes", file=sys.stderr, flush=True)
 
 
-# threads per block x vectors per thread / blocks per CU (0 = unlimited)
-PATTERN_SHAPES = ((256, 2, 0), (256, 2, 1), (256, 1, 1), (256, 1, 2), (128, 2, 1), (128, 2, 2),
-                  (64, 2, 4))
+# threads per block x vectors per thread / blocks per CU (0 = unlimited) / non-temporal
+# stores
+PATTERN_SHAPES = ((256, 2, 0, 0), (256, 2, 1, 0), (256, 1, 1, 0), (128, 2, 2, 0),
+                  (256, 2, 1, 1), (256, 1, 1, 1), (256, 1, 2, 1), (128, 2, 2, 1), (64, 2, 4, 1))
 
 
 def measure_ceiling(bufs, n, reps=20):
@@ -223,16 +224,19 @@ def measure_ceiling(bufs, n, reps=20):
     # the pattern at several launch shapes (threads, vectors per thread, blocks per CU);
     # the ceiling is the best of them
     sweep = {}
-    for t, u, c in PATTERN_SHAPES:
+    for t, u, c, nts in PATTERN_SHAPES:
         ms = timed(lambda: P.neox_probe_update_pattern(ptr["grad"], ptr["half"], ptr["master"],
-                                                       ptr["m"], ptr["v"], n, t, u, c,
+                                                       ptr["m"], ptr["v"], n, t, u, c, nts,
                                                        stream.cuda_stream))
-        sweep[f"{t}x{u}/cu{c}"] = UPDATE_BYTES_PER_PARAM * n / (ms * 1e-3) / 1e9
+        sweep[f"{t}x{u}/cu{c}" + ("/nt" if nts else "")] = \
+            UPDATE_BYTES_PER_PARAM * n / (ms * 1e-3) / 1e9
     best = max(sweep, key=sweep.get)
-    ms_copy = timed(lambda: P.neox_probe_copy(ptr["master"], ptr["m"], 4 * n, stream.cuda_stream))
+    copy = max(8 * n / (timed(lambda: P.neox_probe_copy(ptr["master"], ptr["m"], 4 * n, nts,
+                                                        stream.cuda_stream)) * 1e-3) / 1e9
+               for nts in (0, 1))
     return {"update_pattern_gbps": sweep[best], "update_pattern_shape": best,
             "update_pattern_sweep": {k: round(v, 1) for k, v in sweep.items()},
-            "copy_gbps": 8 * n / (ms_copy * 1e-3) / 1e9}
+            "copy_gbps": copy}
 
 
 def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
@@ -475,8 +479,9 @@ def main():
     if ceiling:
         ceiling["note"] = ("measured on this GPU right after the timed steps: a kernel with the "
                            "update's access pattern and trivial arithmetic, best of the launch "
-                           "shapes swept (threads x vectors per thread / blocks per CU), and a "
-                           "plain copy")
+                           "shapes swept (threads x vectors per thread / blocks per CU / "
+                           "non-temporal stores), and a plain copy (best of plain and "
+                           "non-temporal stores)")
         if kernel_ms:
             ceiling["update_kernel_frac_of_pattern"] = out["roofline"]["achieved"] / \
                 ceiling["update_pattern_gbps"]

@@ -17,9 +17,11 @@
 extern "C" {
 #endif
 
-/* Plain streaming copy: dst[0:bytes) = src[0:bytes), one 16-byte vector per thread.
- * bytes must be a multiple of 16; src and dst must not overlap. */
-int neox_probe_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream);
+/* Plain streaming copy: dst[0:bytes) = src[0:bytes), one 16-byte vector per thread,
+ * stores non-temporal when nt_stores != 0.  bytes must be a multiple of 16; src and dst
+ * must not overlap. */
+int neox_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t nt_stores,
+                    void* hip_stream);
 
 /* The update kernel's memory access pattern with trivial arithmetic: over n elements
  * (a multiple of 8) it reads a 2-byte gradient and three FP32 arrays and writes the
@@ -27,10 +29,11 @@ int neox_probe_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream
  * vectors, in tiles walked last-to-first.  Launch shape: `threads` per block (64, 128,
  * 256 or 512), `vectors` 8-element vectors per thread (1, 2 or 4; a tile is threads x
  * vectors x 8 elements), at most `blocks_per_cu` blocks per CU (0 = as many as fit;
- * 1..16, enforced by reserving LDS).  The arrays' contents are changed. */
+ * 1..16, enforced by reserving LDS), stores non-temporal when nt_stores != 0.  The
+ * arrays' contents are changed. */
 int neox_probe_update_pattern(const void* grad, void* half, float* master, float* exp_avg,
                               float* exp_avg_sq, uint64_t n, int32_t threads, int32_t vectors,
-                              int32_t blocks_per_cu, void* hip_stream);
+                              int32_t blocks_per_cu, int32_t nt_stores, void* hip_stream);
 
 const char* neox_probe_last_error(void);
 

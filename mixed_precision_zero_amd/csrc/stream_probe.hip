@@ -20,15 +20,23 @@ int fail(int code, const char* msg) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+template <bool NTS, typename T>
+__device__ __forceinline__ void put(T* p, T v) {
+    if constexpr (NTS) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <bool NTS>
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
                                                    u32x4* __restrict__ dst, uint64_t nvec) {
     const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < nvec) dst[i] = src[i];
+    if (i < nvec) put<NTS>(dst + i, src[i]);
 }
 
 // The update's access pattern: tiles of NT * U 8-element vectors walked last-to-first,
-// U vectors per thread, the step's arithmetic replaced by a few multiplies.
-template <int NT, int U>
+// U vectors per thread, the step's arithmetic replaced by a few multiplies; NTS:
+// non-temporal stores.
+template <int NT, int U, bool NTS>
 __global__ __launch_bounds__(NT) void pattern_kernel(const u32x4* __restrict__ g,
                                                      u32x4* __restrict__ h,
                                                      f32x4* __restrict__ w,
@@ -53,44 +61,53 @@ __global__ __launch_bounds__(NT) void pattern_kernel(const u32x4* __restrict__ g
         const uint64_t i = base + u * NT + threadIdx.x;
         if (i < nvec) {
             const float gs = __uint_as_float(G[u].x << 16) * 1e-30f;
-            w[2 * i] = W[u][0] + gs; w[2 * i + 1] = W[u][1] + gs;
-            m[2 * i] = M[u][0] * 0.9f; m[2 * i + 1] = M[u][1] * 0.9f;
-            v[2 * i] = V[u][0] * 0.95f; v[2 * i + 1] = V[u][1] * 0.95f;
+            put<NTS>(w + 2 * i, W[u][0] + gs); put<NTS>(w + 2 * i + 1, W[u][1] + gs);
+            put<NTS>(m + 2 * i, M[u][0] * 0.9f); put<NTS>(m + 2 * i + 1, M[u][1] * 0.9f);
+            put<NTS>(v + 2 * i, V[u][0] * 0.95f); put<NTS>(v + 2 * i + 1, V[u][1] * 0.95f);
             const u32x4 hh = {__float_as_uint(W[u][0].x) >> 16, __float_as_uint(W[u][0].z) >> 16,
                               __float_as_uint(W[u][1].x) >> 16, __float_as_uint(W[u][1].z) >> 16};
-            h[i] = hh;
+            put<NTS>(h + i, hh);
         }
     }
 }
 
 template <int NT, int U>
 void launch_pattern(const void* grad, void* half, float* master, float* exp_avg, float* exp_avg_sq,
-                    uint64_t n, uint32_t lds, hipStream_t stream) {
+                    uint64_t n, uint32_t lds, bool nts, hipStream_t stream) {
     const uint64_t nvec = n / 8;
     const uint64_t tiles = (nvec + NT * U - 1) / (NT * U);
-    pattern_kernel<NT, U><<<(uint32_t)tiles, NT, lds, stream>>>(
-        (const u32x4*)grad, (u32x4*)half, (f32x4*)master, (f32x4*)exp_avg, (f32x4*)exp_avg_sq, nvec);
+    if (nts)
+        pattern_kernel<NT, U, true><<<(uint32_t)tiles, NT, lds, stream>>>(
+            (const u32x4*)grad, (u32x4*)half, (f32x4*)master, (f32x4*)exp_avg, (f32x4*)exp_avg_sq, nvec);
+    else
+        pattern_kernel<NT, U, false><<<(uint32_t)tiles, NT, lds, stream>>>(
+            (const u32x4*)grad, (u32x4*)half, (f32x4*)master, (f32x4*)exp_avg, (f32x4*)exp_avg_sq, nvec);
 }
 
 bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
-extern "C" int neox_probe_copy(const void* src, void* dst, uint64_t bytes, void* hip_stream) {
+extern "C" int neox_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t nt_stores,
+                               void* hip_stream) {
     if (!src || !dst || bytes == 0 || bytes % 16 || !a16(src) || !a16(dst))
         return fail(-1, "copy probe: null, unaligned or bad size");
     const uint64_t nvec = bytes / 16;
     const uint64_t grid = (nvec + 255) / 256;
     if (grid > 0xFFFFFFFFull / 256) return fail(-1, "copy probe: too large");
-    copy_kernel<<<(uint32_t)grid, 256, 0, (hipStream_t)hip_stream>>>(
-        (const u32x4*)src, (u32x4*)dst, nvec);
+    if (nt_stores)
+        copy_kernel<true><<<(uint32_t)grid, 256, 0, (hipStream_t)hip_stream>>>(
+            (const u32x4*)src, (u32x4*)dst, nvec);
+    else
+        copy_kernel<false><<<(uint32_t)grid, 256, 0, (hipStream_t)hip_stream>>>(
+            (const u32x4*)src, (u32x4*)dst, nvec);
     return hipGetLastError() == hipSuccess ? 0 : fail(-2, "copy probe launch failed");
 }
 
 extern "C" int neox_probe_update_pattern(const void* grad, void* half, float* master,
                                          float* exp_avg, float* exp_avg_sq, uint64_t n,
                                          int32_t threads, int32_t vectors, int32_t blocks_per_cu,
-                                         void* hip_stream) {
+                                         int32_t nt_stores, void* hip_stream) {
     if (!grad || !half || !master || !exp_avg || !exp_avg_sq || n == 0 || n % 8)
         return fail(-1, "pattern probe: null or n not a positive multiple of 8");
     if (!a16(grad) || !a16(half) || !a16(master) || !a16(exp_avg) || !a16(exp_avg_sq))
@@ -111,7 +128,7 @@ extern "C" int neox_probe_update_pattern(const void* grad, void* half, float* ma
     hipStream_t st = (hipStream_t)hip_stream;
 #define NZP_CASE(T, V)                                                                        \
     if (threads == T && vectors == V) {                                                       \
-        launch_pattern<T, V>(grad, half, master, exp_avg, exp_avg_sq, n, lds, st);            \
+        launch_pattern<T, V>(grad, half, master, exp_avg, exp_avg_sq, n, lds, nt_stores, st); \
         return hipGetLastError() == hipSuccess ? 0 : fail(-2, "pattern probe launch failed"); \
     }
     NZP_CASE(64, 1) NZP_CASE(64, 2) NZP_CASE(64, 4)

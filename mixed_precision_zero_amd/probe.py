@@ -15,10 +15,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build the package first")
         L = C.CDLL(LIB_PATH)
-        L.neox_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]
+        L.neox_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_void_p]
         L.neox_probe_copy.restype = C.c_int
         L.neox_probe_update_pattern.argtypes = [C.c_void_p] * 5 + [C.c_uint64, C.c_int32, C.c_int32,
-                                                                   C.c_int32, C.c_void_p]
+                                                                   C.c_int32, C.c_int32, C.c_void_p]
         L.neox_probe_update_pattern.restype = C.c_int
         L.neox_probe_last_error.argtypes = []
         L.neox_probe_last_error.restype = C.c_char_p
@@ -31,11 +31,11 @@ def _check(rc):
         raise RuntimeError(f"stream probe error {rc}: {lib().neox_probe_last_error().decode()}")
 
 
-def neox_probe_copy(src_ptr, dst_ptr, nbytes, stream_ptr=0):
-    _check(lib().neox_probe_copy(src_ptr, dst_ptr, nbytes, stream_ptr))
+def neox_probe_copy(src_ptr, dst_ptr, nbytes, nt_stores=0, stream_ptr=0):
+    _check(lib().neox_probe_copy(src_ptr, dst_ptr, nbytes, int(nt_stores), stream_ptr))
 
 
 def neox_probe_update_pattern(grad, half, master, exp_avg, exp_avg_sq, n, threads=256, vectors=2,
-                              blocks_per_cu=0, stream_ptr=0):
+                              blocks_per_cu=0, nt_stores=0, stream_ptr=0):
     _check(lib().neox_probe_update_pattern(grad, half, master, exp_avg, exp_avg_sq, n, threads,
-                                           vectors, blocks_per_cu, stream_ptr))
+                                           vectors, blocks_per_cu, int(nt_stores), stream_ptr))
