@@ -196,12 +196,10 @@ __device__ __forceinline__ void sq8(const uint4 q, float inv, double& a0, double
     }
 }
 
+// This block's sum of squares over its chunks (every thread gets the value).
 template <int DT>
-__global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ chunks,
-                                                      uint32_t nchunks,
-                                                      const DevState* __restrict__ st,
-                                                      double* __restrict__ partial) {
-    const float inv = st->inv;
+__device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, uint32_t nchunks,
+                                             float inv) {
     double a0 = 0.0, a1 = 0.0;
     for (uint32_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const Chunk* ch = chunks + c;
@@ -228,7 +226,15 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ 
             a0 = __builtin_fma(x, x, a0);
         }
     }
-    const double s = block_sum<kBlock>(a0 + a1);
+    return block_sum<kBlock>(a0 + a1);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ chunks,
+                                                      uint32_t nchunks,
+                                                      const DevState* __restrict__ st,
+                                                      double* __restrict__ partial) {
+    const double s = norm_block<DT>(chunks, nchunks, st->inv);
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
@@ -242,21 +248,23 @@ __device__ __forceinline__ bool f32_finite(float x) {
     return (__float_as_uint(x) & 0x7F800000u) != 0x7F800000u;
 }
 
-constexpr int kFinalizeBlock = 1024;
+// Block size of every fixed-order sum of the partials (the finalize and the split step's
+// reduce), so both add in the same order.
+constexpr int kFinalizeBlock = kBlock;
 
 // Fixed-order sum of the norm pass's partials by one block of kFinalizeBlock threads:
-// thread t owns partials t, t + 1024, ...; four independent loads per round keep the
-// one-block read of up to a few MB of partials latency-tolerant.
+// thread t owns partials t, t + kFinalizeBlock, ... in that order; eight independent
+// loads per round keep the one-block read latency-tolerant.
 __device__ __forceinline__ double sum_partials(const double* __restrict__ partial, uint32_t nparts) {
+    constexpr int R = 8;
     double acc = 0.0;
     uint32_t i = threadIdx.x;
-    for (; i + 3 * kFinalizeBlock < nparts; i += 4 * kFinalizeBlock) {
-        const double p0 = partial[i], p1 = partial[i + kFinalizeBlock];
-        const double p2 = partial[i + 2 * kFinalizeBlock], p3 = partial[i + 3 * kFinalizeBlock];
-        acc += p0;
-        acc += p1;
-        acc += p2;
-        acc += p3;
+    for (; i + (R - 1) * kFinalizeBlock < nparts; i += R * kFinalizeBlock) {
+        double p[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) p[r] = partial[i + r * kFinalizeBlock];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc += p[r];
     }
     for (; i < nparts; i += kFinalizeBlock) acc += partial[i];
     return block_sum<kFinalizeBlock>(acc);
@@ -295,15 +303,10 @@ __global__ void set_state_kernel(DevState* __restrict__ st, float scale, int32_t
     st->inv = unscale_factor(predivide, dp, scale);
 }
 
-__global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* __restrict__ partial,
-                                                                  uint32_t nparts,
-                                                                  const double* __restrict__ sumsq_in,
-                                                                  DevState* __restrict__ st,
-                                                                  FinalizeArgs a) {
-    // the squared norm: this handle's own partials, or a value summed over the ranks
-    const double sumsq = sumsq_in ? *sumsq_in : sum_partials(partial, nparts);
-    if (threadIdx.x != 0) return;
-
+// The step's decisions from its squared norm (one thread): skip, clip coefficient, step
+// count, bias corrections and the loss-scale state machine, written to the state block.
+__device__ __forceinline__ void finalize_state(double sumsq, DevState* __restrict__ st,
+                                               const FinalizeArgs& a) {
     float scale = st->loss_scale;
     const float inv_used = st->inv;
     if (!f64_finite(sumsq)) {
@@ -347,6 +350,16 @@ __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* 
     }
     st->loss_scale = scale;
     st->inv = unscale_factor(a.predivide_factor, a.dp_world_size, scale);
+}
+
+__global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* __restrict__ partial,
+                                                                  uint32_t nparts,
+                                                                  const double* __restrict__ sumsq_in,
+                                                                  DevState* __restrict__ st,
+                                                                  FinalizeArgs a) {
+    // the squared norm: this handle's own partials, or a value summed over the ranks
+    const double sumsq = sumsq_in ? *sumsq_in : sum_partials(partial, nparts);
+    if (threadIdx.x == 0) finalize_state(sumsq, st, a);
 }
 
 // ------------------------------------------------------------------------------------
