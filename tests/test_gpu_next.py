@@ -57,19 +57,20 @@ def test_split_step_equals_step_on_one_rank():
         assert torch.equal(outs[0][k], outs[1][k]), k
 
 
-def test_split_step_four_ranks_match_the_global_oracle():
-    """Four ZeRO-1 ranks of one model on this GPU: each runs step_local, the four local
-    squared norms are summed in rank order on the host and handed to every rank's
-    step_apply.  Decisions equal the oracle's on the whole model every step, clipping
-    is active, an inf in one rank's shard skips every rank, and every rank's elements
-    match the oracle's global step."""
+@pytest.mark.parametrize("D", [4, 8])
+def test_split_step_ranks_match_the_global_oracle(D):
+    """D ZeRO-1 ranks of one model on this GPU, one after another: each runs step_local,
+    the D local squared norms are summed in rank order on the host and handed to every
+    rank's step_apply.  Decisions equal the oracle's on the whole model every step,
+    clipping is active, an inf in one rank's shard skips every rank, and every rank's
+    elements match the oracle's global step."""
     tensors = [(50_000, True), (1_000, False), (120_011, True), (7, False), (30_000, True),
                (2_048, False), (64_000, True)]
-    D, A = 4, 64
+    A = 64
     numel = [n for n, _ in tensors]
     decay = [d for _, d in tensors]
     hy = W.Hyper(clip_norm=0.02)
-    full = W.Workload("split4", 911, tensors, hy, grad_sigma=1e-4)
+    full = W.Workload(f"split{D}", 911, tensors, hy, grad_sigma=1e-4)
     total = full.numel
     stream = torch.cuda.current_stream().cuda_stream
 
