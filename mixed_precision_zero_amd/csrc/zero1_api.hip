@@ -54,6 +54,10 @@ int hip_fail(hipError_t e, const char* what) {
 #ifndef NZ1_FLAT_BLOCKS_PER_CU
 #define NZ1_FLAT_BLOCKS_PER_CU 2
 #endif
+// momentum SGD moves 20 B/param over seven streams and prefers more blocks in flight
+#ifndef NZ1_FLAT_BLOCKS_PER_CU_SGD
+#define NZ1_FLAT_BLOCKS_PER_CU_SGD 4
+#endif
 constexpr uint32_t kDefaultChunk = NZ1_UPDATE_CHUNK;
 constexpr uint32_t kNormChunk = NZ1_NORM_CHUNK;
 
@@ -478,7 +482,8 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     };
     h->update_lds = reserve(NZ1_UPDATE_BLOCKS_PER_CU);
     h->norm_lds = reserve(NZ1_NORM_BLOCKS_PER_CU);
-    h->flat_lds = reserve(NZ1_FLAT_BLOCKS_PER_CU);
+    h->flat_lds = reserve(cfg->optimizer == NEOX_OPT_SGD ? NZ1_FLAT_BLOCKS_PER_CU_SGD
+                                                         : NZ1_FLAT_BLOCKS_PER_CU);
     h->nnorm = (uint32_t)norm_table.size();
     // norm pass: one block per norm chunk unless a smaller striding grid is requested
     uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : h->nnorm;
