@@ -261,3 +261,43 @@ def test_flat_equals_chunked_bitwise(optimizer):
     assert states[0] == states[1] and states[0][2] == 2
     for k in outs[0]:
         assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+def test_argument_errors_enqueue_nothing():
+    """Calls rejected by validation (non-finite lr, misaligned or null device doubles,
+    wrong telemetry length, bad timing requests) return NEOX_EINVAL and leave the state
+    and every array untouched."""
+    import ctypes as C
+    w = _custom("errors", [5000, 3], [True, False])
+    shard = DeviceShard(w)
+    shard.init_()
+    shard.grads_(0, w.hyper.init_scale)
+    stream = torch.cuda.current_stream().cuda_stream
+    h = Z.neox_zero1_create(lib_config(w), shard.neox_segments(), stream)
+    L = Z.lib()
+    try:
+        before = _outputs(shard)
+        st0 = Z.neox_scaler_state(h)
+        d = torch.zeros(2, dtype=torch.float64, device="cuda")
+        for lr in (float("nan"), float("inf"), float("-inf")):
+            assert L.neox_zero1_step(C.c_void_p(h), C.c_float(lr), C.c_void_p(stream)) == Z.NEOX_EINVAL
+            assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(d.data_ptr()), C.c_float(lr),
+                                           C.c_void_p(stream)) == Z.NEOX_EINVAL
+        odd = d.data_ptr() + 4
+        assert L.neox_zero1_step_local(C.c_void_p(h), C.c_void_p(odd), C.c_void_p(stream)) == Z.NEOX_EINVAL
+        assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(odd), C.c_float(1e-3),
+                                       C.c_void_p(stream)) == Z.NEOX_EINVAL
+        assert L.neox_zero1_step_local(C.c_void_p(h), None, C.c_void_p(stream)) == Z.NEOX_EINVAL
+        out = (C.c_double * 2)()
+        assert L.neox_zero1_segment_sumsq(C.c_void_p(h), out, 2) == Z.NEOX_EINVAL   # telemetry off
+        for steps, upd in ((0, 0), (-1, 0), (4, 2)):
+            assert L.neox_zero1_timing_begin(C.c_void_p(h), steps, upd) == Z.NEOX_EINVAL
+        assert Z.neox_zero1_update_path(h) in (Z.NEOX_PATH_FLAT, Z.NEOX_PATH_CHUNKED)
+        st1 = Z.neox_scaler_state(h)
+        assert (st1.step, st1.skipped_total, st1.loss_scale, st1.good_steps) == \
+            (st0.step, st0.skipped_total, st0.loss_scale, st0.good_steps)
+        after = _outputs(shard)
+        for k in before:
+            assert torch.equal(before[k], after[k]), k
+    finally:
+        Z.neox_zero1_destroy(h)
