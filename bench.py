@@ -73,7 +73,7 @@ def summarize_trace(args):
     per_param = {"update_kernel": UPDATE_BYTES_PER_PARAM, "norm_kernel": 2}
     lines = [
         f"# rocprofv3 kernel trace of the ZeRO-1 step on {args.workload} ({n} params), MI355X (gfx950).",
-        "# Commands (repository root on the GPU box):",
+        "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py "
         f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline > <log>",
         f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} --bench-log <log>",
@@ -147,7 +147,7 @@ def summarize_pmc(args):
     traffic = (fetch * ff + write * fw) * 1024.0
     lines = [
         f"# HBM traffic of the update on {args.workload} ({n} params), from rocprofv3 PMC.",
-        "# Commands (run from the repository root on the MI355X box):",
+        "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- python3 bench.py "
         f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events",
         "#   rocprofv3 --pmc WRITE_SIZE -d <write_dir> ... (same program)",
@@ -326,8 +326,8 @@ def main():
         copy_probe(args.copy_probe_only)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the step is per-rank work and multi-GPU runs are not part of it", file=sys.stderr)
+        print(f"bench.py: the step is one rank's work and is measured on one GPU only "
+              f"(--gpus {args.gpus} requested); multi-GPU runs are not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -8,7 +8,7 @@
 
 namespace nz1 {
 
-constexpr int kBlock = 256;   // threads per block: 4 wave64s
+constexpr int kBlock = 256;   // threads per block of the norm, finalize and telemetry kernels
 constexpr int kVec = 8;       // elements per thread-vector: one 16-byte load of halves
 
 enum : uint32_t {
@@ -48,7 +48,7 @@ struct alignas(64) DevState {
     // handed from the finalize to the passes
     float inv;                   // fp32(f / (D * S)) for the next norm pass
     int32_t pad_[3];
-    // what the update reads, in one 16-byte block (one scalar load)
+    // what the update reads, in one 16-byte block (one scalar load in the chunked update)
     int32_t skip;                // this step's decision
     float gscale;                // this step's unscale factor times clip coefficient
     float rbc1;                  // 1 / (1 - beta1^t)

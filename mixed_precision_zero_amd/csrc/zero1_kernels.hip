@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* 
 }
 
 // ------------------------------------------------------------------------------------
-// update: fused unscale + clip + AdamW + cast, one block per chunk
+// update: fused unscale + clip + AdamW + cast, one block per chunk or flat tile
 // ------------------------------------------------------------------------------------
 struct Coefs {
     float gs, rbc1, rsbc2;
