@@ -301,3 +301,19 @@ def test_argument_errors_enqueue_nothing():
             assert torch.equal(before[k], after[k]), k
     finally:
         Z.neox_zero1_destroy(h)
+
+
+@pytest.mark.parametrize("sizes", [[2048], [1000, 1048], [4096, 7, 2041, 2048], [8, 8192 - 8]],
+                         ids=["one_tile", "two_segments", "three_tiles", "four_tiles"])
+def test_flat_shard_of_whole_tiles(sizes):
+    """Flat shards that end exactly on a tile boundary (no short last tile), with a flag
+    change inside a tile, against the oracle, one step skipped."""
+    decays = [i % 2 == 0 for i in range(len(sizes))]
+    w = _custom("whole_tiles", sizes, decays, weight_decay=0.5)
+    w.injections = {1: [(sum(sizes) - 1, "nan")]}
+    shard = DeviceShard(w, flat=True)
+    plan = Z.neox_zero1_plan(lib_config(w), shard.neox_segments(), tables=False)[0]
+    assert plan.update_path == Z.NEOX_PATH_FLAT and w.numel % plan.tile_elems == 0
+    log(f"case whole tiles {sizes}")
+    chk = run_sequence(w, 3, shard=shard, where=f" whole tiles {sizes}")
+    assert chk.ost.skipped_total == 1
