@@ -99,7 +99,7 @@ def summarize_trace(args):
             last = [ln for ln in fh if ln.startswith("{")][-1]
         b = json.loads(last)
         k = b.get("kernel_avg_ms", {})
-        lines.append(f"bench.py in the same run (HIP events on the step's stream): update avg "
+        lines.append(f"bench.py in the same run (dispatch-stamped HIP events): update avg "
                      f"{k.get('update', 0) * 1e3:.1f} us, norm {k.get('norm', 0) * 1e3:.1f} us, "
                      f"finalize {k.get('finalize', 0) * 1e3:.1f} us, step "
                      f"{b['ms_per_step'] * 1e3:.1f} us wall")

@@ -245,12 +245,13 @@ int neox_scaler_set(neox_zero1* h, const neox_scaler_state_t* st, void* hip_stre
 int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg);
 
 /* Per-kernel timing for profiling.  neox_zero1_timing_begin(h, max_steps, update_only)
- * makes the next max_steps calls of neox_zero1_step record HIP events on their stream:
- * around each of the three kernels, or (update_only = 1) around the update kernel only,
- * which keeps the recording's own cost out of the other kernels.
- * neox_zero1_timing_end() waits, writes the summed durations in milliseconds of the
- * norm pass, the finalize and the update to ms_sums[3] (host; the first two are 0 with
- * update_only), the number of recorded steps to *steps, and stops recording.
+ * makes the next max_steps calls of neox_zero1_step time their kernels: each of the
+ * three kernels, or (update_only = 1) the update kernel only, is launched with a pair of
+ * HIP events that its own dispatch stamps with its start and end (no marker packets are
+ * added to the stream).  neox_zero1_timing_end() waits, writes the summed kernel
+ * durations in milliseconds of the norm pass, the finalize and the update to ms_sums[3]
+ * (host; the first two are 0 with update_only), the number of recorded steps to *steps,
+ * and stops recording.
  * Errors: NEOX_EINVAL, NEOX_ENOMEM, NEOX_EHIP. */
 int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only);
 int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);

@@ -61,8 +61,9 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr uint32_t kDefaultChunk = NZ1_UPDATE_CHUNK;
 constexpr uint32_t kNormChunk = NZ1_NORM_CHUNK;
 
+// start / stop of the norm, finalize and update kernels of one recorded step
 struct TimingSlot {
-    hipEvent_t ev[4];
+    hipEvent_t ev[6];
 };
 
 }  // namespace
@@ -590,22 +591,23 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 }
 
 // norm pass (+ per-segment sums when enabled)
-static hipError_t enqueue_norm(neox_zero1* h, hipStream_t stream) {
+static hipError_t enqueue_norm(neox_zero1* h, hipStream_t stream, const KernelTiming& t = {}) {
     hipError_t e = launch_norm(h->cfg.dtype, h->d_norm_chunks, h->nnorm, h->norm_blocks,
-                               h->d_state, h->d_partial, h->norm_lds, stream);
+                               h->d_state, h->d_partial, h->norm_lds, stream, t);
     if (e == hipSuccess && h->cfg.segment_norms)
         e = launch_segment_sumsq(h->d_partial, h->d_seg_range, h->nseg, h->d_seg_sumsq, stream);
     return e;
 }
 
-static hipError_t enqueue_update(neox_zero1* h, float lr, hipStream_t stream) {
+static hipError_t enqueue_update(neox_zero1* h, float lr, hipStream_t stream,
+                                 const KernelTiming& t = {}) {
     UpdateArgs u = h->upd_base;
     u.lr = lr;
     if (h->flat)
         return launch_flat_update(h->cfg.dtype, h->cfg.optimizer, h->span, h->d_state, u,
-                                  h->flat_lds, stream);
+                                  h->flat_lds, stream, t);
     return launch_update(h->cfg.dtype, h->cfg.optimizer, h->d_chunks, h->nchunks, h->d_state, u,
-                         h->update_lds, stream);
+                         h->update_lds, stream, t);
 }
 
 extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
@@ -616,14 +618,16 @@ extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
     if (h->timing_used < (int64_t)h->timing.size()) ts = &h->timing[h->timing_used++];
 
     const bool all = ts && !h->timing_update_only;
-    hipError_t e = hipSuccess;
-    if (all) e = hipEventRecord(ts->ev[0], stream);
-    if (e == hipSuccess) e = enqueue_norm(h, stream);
-    if (e == hipSuccess && all) e = hipEventRecord(ts->ev[1], stream);
-    if (e == hipSuccess) e = launch_finalize(h->d_partial, h->norm_blocks, nullptr, h->d_state, h->fin, stream);
-    if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[2], stream);
-    if (e == hipSuccess) e = enqueue_update(h, lr, stream);
-    if (e == hipSuccess && ts) e = hipEventRecord(ts->ev[3], stream);
+    KernelTiming tn, tf, tu;
+    if (all) {
+        tn = {ts->ev[0], ts->ev[1]};
+        tf = {ts->ev[2], ts->ev[3]};
+    }
+    if (ts) tu = {ts->ev[4], ts->ev[5]};
+    hipError_t e = enqueue_norm(h, stream, tn);
+    if (e == hipSuccess)
+        e = launch_finalize(h->d_partial, h->norm_blocks, nullptr, h->d_state, h->fin, stream, tf);
+    if (e == hipSuccess) e = enqueue_update(h, lr, stream, tu);
     h->last_stream = stream;
     if (e != hipSuccess) return hip_fail(e, "step launch");
     return NEOX_OK;
@@ -734,11 +738,11 @@ extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* st
     ms_sums[0] = ms_sums[1] = ms_sums[2] = 0.0;
     for (int64_t i = 0; i < h->timing_used; ++i) {
         auto& s = h->timing[i];
-        hipError_t r = hipEventSynchronize(s.ev[3]);
+        hipError_t r = hipEventSynchronize(s.ev[5]);
         if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
         for (int k = h->timing_update_only ? 2 : 0; k < 3; ++k) {
             float ms = 0.0f;
-            r = hipEventElapsedTime(&ms, s.ev[k], s.ev[k + 1]);
+            r = hipEventElapsedTime(&ms, s.ev[2 * k], s.ev[2 * k + 1]);
             if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
             ms_sums[k] += ms;
         }

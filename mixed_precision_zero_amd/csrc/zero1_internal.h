@@ -99,12 +99,20 @@ struct UpdateArgs {
     float b1, omb1, b2, omb2, eps, wd, lr;
 };
 
+// Optional timing of one launch: both null, or two events that receive the kernel's own
+// start and stop time from its dispatch (no marker packets between kernels).
+struct KernelTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
                        const DevState* st, double* partial, uint32_t lds_reserve,
-                       hipStream_t stream);
+                       hipStream_t stream, const KernelTiming& t = {});
 hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
-                           DevState* st, const FinalizeArgs& a, hipStream_t stream);
+                           DevState* st, const FinalizeArgs& a, hipStream_t stream,
+                           const KernelTiming& t = {});
 hipError_t launch_reduce(const double* partial, uint32_t nparts, double* out, hipStream_t stream);
 hipError_t launch_segment_sumsq(const double* partial, const uint32_t* range, uint32_t nseg,
                                 double* out, hipStream_t stream);
@@ -113,9 +121,10 @@ hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64
                             hipStream_t stream);
 hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
                          const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
-                         hipStream_t stream);
+                         hipStream_t stream, const KernelTiming& t = {});
 hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const DevState* st,
-                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream);
+                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream,
+                              const KernelTiming& t = {});
 
 // The unscale factor for scale s, computed in double and rounded once to FP32; the
 // host (initial state) and the finalize kernel evaluate the same expression.

@@ -22,6 +22,8 @@
 // (Micikevicius et al. 2018).
 #include "zero1_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace nz1 {
 
 // ------------------------------------------------------------------------------------
@@ -723,19 +725,29 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
 // ------------------------------------------------------------------------------------
 constexpr int kUpdateUnroll = NZ1_UPDATE_UNROLL;
 
+// One launch, timed through its own dispatch when t carries events.
+template <typename... Params, typename... Args>
+static void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t lds,
+                   hipStream_t stream, const KernelTiming& t, Args... args) {
+    if (t.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, t.start, t.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+}
+
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
                        const DevState* st, double* partial, uint32_t lds_reserve,
-                       hipStream_t stream) {
-    if (dtype == 1)
-        norm_kernel<1><<<blocks, kBlock, lds_reserve, stream>>>(chunks, nchunks, st, partial);
-    else
-        norm_kernel<2><<<blocks, kBlock, lds_reserve, stream>>>(chunks, nchunks, st, partial);
+                       hipStream_t stream, const KernelTiming& t) {
+    launch(dtype == 1 ? norm_kernel<1> : norm_kernel<2>, dim3(blocks), dim3(kBlock), lds_reserve,
+           stream, t, chunks, nchunks, st, partial);
     return hipGetLastError();
 }
 
 hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
-                           DevState* st, const FinalizeArgs& a, hipStream_t stream) {
-    finalize_kernel<<<1, kFinalizeBlock, 0, stream>>>(partial, nparts, sumsq_in, st, a);
+                           DevState* st, const FinalizeArgs& a, hipStream_t stream,
+                           const KernelTiming& t) {
+    launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), 0, stream, t, partial, nparts, sumsq_in,
+           st, a);
     return hipGetLastError();
 }
 
@@ -760,28 +772,26 @@ hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64
 
 template <int OPT>
 static void launch_update_opt(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
-                              const UpdateArgs& a, uint32_t lds, hipStream_t stream) {
-    if (dtype == 1)
-        update_kernel<1, kUpdateUnroll, OPT><<<nchunks, kUpdateBlock, lds, stream>>>(chunks, nchunks, st, a);
-    else
-        update_kernel<2, kUpdateUnroll, OPT><<<nchunks, kUpdateBlock, lds, stream>>>(chunks, nchunks, st, a);
+                              const UpdateArgs& a, uint32_t lds, hipStream_t stream,
+                              const KernelTiming& t) {
+    launch(dtype == 1 ? update_kernel<1, kUpdateUnroll, OPT> : update_kernel<2, kUpdateUnroll, OPT>,
+           dim3(nchunks), dim3(kUpdateBlock), lds, stream, t, chunks, nchunks, st, a);
 }
 
 template <int OPT>
 static void launch_flat_opt(int dtype, const FlatSpan& f, const DevState* st, const UpdateArgs& a,
-                            uint32_t lds, hipStream_t stream) {
-    if (dtype == 1)
-        flat_update_kernel<1, OPT><<<f.ntiles, kFlatBlock, lds, stream>>>(f, f.tile_word, f.change, st, a);
-    else
-        flat_update_kernel<2, OPT><<<f.ntiles, kFlatBlock, lds, stream>>>(f, f.tile_word, f.change, st, a);
+                            uint32_t lds, hipStream_t stream, const KernelTiming& t) {
+    launch(dtype == 1 ? flat_update_kernel<1, OPT> : flat_update_kernel<2, OPT>, dim3(f.ntiles),
+           dim3(kFlatBlock), lds, stream, t, f, f.tile_word, f.change, st, a);
 }
 
 hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const DevState* st,
-                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream) {
+                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream,
+                              const KernelTiming& t) {
     if (optimizer == 1)
-        launch_flat_opt<1>(dtype, f, st, a, lds_reserve, stream);
+        launch_flat_opt<1>(dtype, f, st, a, lds_reserve, stream, t);
     else
-        launch_flat_opt<0>(dtype, f, st, a, lds_reserve, stream);
+        launch_flat_opt<0>(dtype, f, st, a, lds_reserve, stream, t);
     return hipGetLastError();
 }
 
@@ -789,11 +799,11 @@ hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const
 // blocks share a CU (fewer tiles in flight keep the chip's open DRAM rows few).
 hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
                          const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
-                         hipStream_t stream) {
+                         hipStream_t stream, const KernelTiming& t) {
     if (optimizer == 1)
-        launch_update_opt<1>(dtype, chunks, nchunks, st, a, lds_reserve, stream);
+        launch_update_opt<1>(dtype, chunks, nchunks, st, a, lds_reserve, stream, t);
     else
-        launch_update_opt<0>(dtype, chunks, nchunks, st, a, lds_reserve, stream);
+        launch_update_opt<0>(dtype, chunks, nchunks, st, a, lds_reserve, stream, t);
     return hipGetLastError();
 }
 
