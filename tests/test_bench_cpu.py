@@ -1,0 +1,99 @@
+"""bench.py's measurement plumbing on the CPU: the rocprofv3 summaries it writes from
+counter and kernel-statistics CSV files, the traffic it reads back (and refuses when the
+kernel sources or the workload differ), and the one-GPU guard."""
+import argparse
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+N215 = 215_000_000
+
+
+def _counter_csv(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, counter, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def _pmc_args(tmp_path, out):
+    upd = "void nz1::flat_update_kernel<1, 0>(nz1::FlatSpan, unsigned int const*)"
+    copy = "void at::native::MulFunctor<float>(float)"
+    _counter_csv(tmp_path / "f", [(upd, "FETCH_SIZE", 1000.0), (upd, "FETCH_SIZE", 1002.0),
+                                  ("void nz1::norm_kernel<1>()", "FETCH_SIZE", 5.0)])
+    _counter_csv(tmp_path / "w", [(upd, "WRITE_SIZE", 3000.0), (upd, "WRITE_SIZE", 3000.0)])
+    _counter_csv(tmp_path / "cf", [(copy, "FETCH_SIZE", 512.0)])      # 1 MiB read, counted as 512 KiB
+    _counter_csv(tmp_path / "cw", [(copy, "WRITE_SIZE", 1024.0)])
+    return argparse.Namespace(pmc_fetch=str(tmp_path / "f"), pmc_write=str(tmp_path / "w"),
+                              pmc_copy_fetch=str(tmp_path / "cf"),
+                              pmc_copy_write=str(tmp_path / "cw"), copy_bytes=1 << 20,
+                              workload="neox20b_shard_215m", out=str(out))
+
+
+def test_pmc_summary_and_traffic_readback(tmp_path, monkeypatch, capsys):
+    out = tmp_path / "summary.txt"
+    bench.summarize_pmc(_pmc_args(tmp_path, out))
+    text = out.read_text()
+    vals = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith("#"))
+    assert vals["kernel"] == "nz1::flat_update_kernel<1, 0>"
+    assert float(vals["fetch_kib_per_dispatch"]) == 1001.0 and vals["update_dispatches"] == "2"
+    assert float(vals["copy_factor_fetch"]) == 2.0 and float(vals["copy_factor_write"]) == 1.0
+    want = 1024.0 * (1001.0 * 2.0 + 3000.0 * 1.0)
+    assert float(vals["traffic_bytes_per_dispatch"]) == round(want)
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(out))
+    assert bench.read_traffic("neox20b_shard_215m", N215) == want
+    assert bench.read_traffic("tiny_1m", 1 << 20) is None              # other workload
+    monkeypatch.setattr(bench, "kernel_sha", lambda: "0" * 64)
+    assert bench.read_traffic("neox20b_shard_215m", N215) is None      # other kernel sources
+
+
+def test_pmc_summary_needs_the_update_kernel(tmp_path):
+    args = _pmc_args(tmp_path, tmp_path / "s.txt")
+    _counter_csv(tmp_path / "w", [("void nz1::norm_kernel<1>()", "WRITE_SIZE", 1.0)])
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(args)
+
+
+def test_trace_summary(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "t_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
+                                          "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow(dict(Name="void nz1::flat_update_kernel<1, 0>(nz1::FlatSpan)", Calls=43,
+                        TotalDurationNs=43 * 1_050_000, AverageNs=1_050_000.0, Percentage=90,
+                        MinNs=1_000_000, MaxNs=1_100_000, StdDev=1))
+        w.writerow(dict(Name="void nz1::norm_kernel<1>(nz1::Chunk const*)", Calls=43,
+                        TotalDurationNs=43 * 66_000, AverageNs=66_000.0, Percentage=6,
+                        MinNs=60_000, MaxNs=70_000, StdDev=1))
+        w.writerow(dict(Name="void at::native::normal_kernel()", Calls=5, TotalDurationNs=10,
+                        AverageNs=2.0, Percentage=0, MinNs=1, MaxNs=3, StdDev=0))
+    log = tmp_path / "bench.log"
+    log.write_text("[bench] noise\n" + json.dumps({"ms_per_step": 1.12, "kernel_avg_ms": {
+        "norm": 0.066, "finalize": 0.005, "update": 1.05}}) + "\n")
+    out = tmp_path / "trace.txt"
+    bench.summarize_trace(argparse.Namespace(trace=str(d), workload="neox20b_shard_215m",
+                                             trace_steps=20, bench_log=str(log), out=str(out)))
+    text = out.read_text()
+    assert "normal_kernel" not in text
+    assert f"nz1::flat_update_kernel: {28 * N215} algorithmic bytes per launch / 1050.0 us" in text
+    assert f"= {28 * N215 / 1050e-6 / 1e9:.1f} GB/s" in text
+    assert f"nz1::norm_kernel: {2 * N215} algorithmic bytes per launch / 66.0 us" in text
+    assert "update avg 1050.0 us" in text and "step 1120.0 us wall" in text
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
