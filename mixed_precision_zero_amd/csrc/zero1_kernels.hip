@@ -305,12 +305,30 @@ __global__ void set_state_kernel(DevState* __restrict__ st, float scale, int32_t
     st->inv = unscale_factor(predivide, dp, scale);
 }
 
+// b^t for an integer t >= 1 by binary exponentiation: at most ~2 log2(t) roundings
+// (a few ulps), and a short dependent chain for the one thread that runs it.
+__device__ __forceinline__ double ipow(double b, int64_t t) {
+    double r = 1.0;
+    while (t) {
+        if (t & 1) r *= b;
+        b *= b;
+        t >>= 1;
+    }
+    return r;
+}
+
 // The step's decisions from its squared norm (one thread): skip, clip coefficient, step
 // count, bias corrections and the loss-scale state machine, written to the state block.
+// The state is read once up front (one batch of scalar loads) and written at the end.
 __device__ __forceinline__ void finalize_state(double sumsq, DevState* __restrict__ st,
                                                const FinalizeArgs& a) {
-    float scale = st->loss_scale;
+    const float scale0 = st->loss_scale;
     const float inv_used = st->inv;
+    const int32_t good0 = st->good_steps;
+    const int64_t step0 = st->step;
+    const int64_t skipped0 = st->skipped_total;
+    const int32_t consecutive0 = st->consecutive_overflows;
+    float scale = scale0;
     if (!f64_finite(sumsq)) {
         // overflow: skip, back off (not below the floor), restart the clean count
         st->skip = 1;
@@ -319,8 +337,8 @@ __device__ __forceinline__ void finalize_state(double sumsq, DevState* __restric
             scale = s < a.min_scale ? a.min_scale : s;
         }
         st->good_steps = 0;
-        st->consecutive_overflows += 1;
-        st->skipped_total += 1;
+        st->consecutive_overflows = consecutive0 + 1;
+        st->skipped_total = skipped0 + 1;
         st->last_skipped = 1;
         st->last_sumsq = 0.0;
         st->last_grad_norm = __builtin_inff();
@@ -329,15 +347,15 @@ __device__ __forceinline__ void finalize_state(double sumsq, DevState* __restric
         const double norm = __builtin_sqrt(sumsq);
         double coef = 1.0;
         if (a.clip_norm > 0.0 && norm > a.clip_norm) coef = a.clip_norm / norm;
-        const int64_t t = st->step + 1;
-        const double bc1 = 1.0 - pow(a.beta1, (double)t);
-        const double bc2 = 1.0 - pow(a.beta2, (double)t);
+        const int64_t t = step0 + 1;
+        const double bc1 = 1.0 - ipow(a.beta1, t);
+        const double bc2 = 1.0 - ipow(a.beta2, t);
         st->skip = 0;
         st->gscale = (float)((double)inv_used * coef);
         st->rbc1 = (float)(1.0 / bc1);
         st->rsbc2 = (float)(1.0 / __builtin_sqrt(bc2));
         st->step = t;
-        int32_t good = st->good_steps + 1;
+        int32_t good = good0 + 1;
         if (a.dynamic && good >= a.growth_interval) {
             const float s = (float)((double)scale * a.growth_factor);
             if (f32_finite(s)) scale = s;

@@ -189,6 +189,20 @@ def test_resume_equals_continuous():
         assert torch.equal(oa[k], ob[k]), k
 
 
+@pytest.mark.parametrize("t0", [996, 4093, 123_457, 2 ** 40 + 3])
+def test_parity_after_restored_step_count(t0):
+    """A handle created at a large step count (a restored run): the bias corrections
+    1 - beta^t of the next steps match the oracle's.  With both betas at 0.999, beta^t is
+    about 0.37 and 0.017 in the first two cases (long exponent chains that still matter),
+    negligible in the third and zero (underflow) in the last."""
+    w = _custom(f"restored{t0}", [40_000, 3, 9000], [True, False, True])
+    log(f"case restored step {t0}")
+    for beta1, beta2 in ((0.9, 0.95), (0.999, 0.999)):
+        w.hyper.beta1, w.hyper.beta2 = beta1, beta2
+        chk = run_sequence(w, 3, init_step=t0, where=f" t0={t0} betas={beta1},{beta2}")
+        assert chk.ost.step == t0 + 3
+
+
 def _path(w, shard, **over):
     h = Z.neox_zero1_create(lib_config(w, **over), shard.neox_segments(),
                             torch.cuda.current_stream().cuda_stream)
