@@ -75,7 +75,7 @@ def summarize_trace(args):
         f"# rocprofv3 kernel trace of the ZeRO-1 step on {args.workload} ({n} params), MI355X (gfx950).",
         "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py "
-        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline > <log>",
+        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline --skip-steps 0 > <log>",
         f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} --bench-log <log>",
         f"# Calls = 3 warm-up + {args.trace_steps} timed steps (update-kernel events only) + 20 steps",
         "# with events around every kernel; the torch kernels that draw the synthetic inputs and the",
@@ -149,7 +149,7 @@ def summarize_pmc(args):
         f"# HBM traffic of the update on {args.workload} ({n} params), from rocprofv3 PMC.",
         "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- python3 bench.py "
-        f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events",
+        f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events --skip-steps 0",
         "#   rocprofv3 --pmc WRITE_SIZE -d <write_dir> ... (same program)",
         f"#   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch_dir> --output-format csv -- python3 bench.py "
         f"--copy-probe-only {args.copy_bytes}",
@@ -280,6 +280,39 @@ def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
                       f"{spent:.1f} s of single-thread oracle time (fp64 scalar C, -O2)"}
 
 
+def time_skipped_steps(Z, h, grad, one_step, steps, events):
+    """Steps whose gradient holds an inf at element 0: the norm pass still reads the whole
+    gradient, the finalize decides to skip, and the update's blocks read the decision and
+    return.  Returns wall ms per step and, with events, the per-kernel averages.  The
+    element is restored afterwards; the handle's scaler state keeps the skips."""
+    import torch
+
+    before = Z.neox_scaler_state(h).skipped_total
+    saved = grad[0:1].clone()
+    grad[0:1].fill_(float("inf"))
+    one_step()
+    one_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kernels = None
+    if events:
+        Z.neox_zero1_timing_begin(h, steps)
+        for _ in range(steps):
+            one_step()
+        sums, k = Z.neox_zero1_timing_end(h)
+        kernels = {"norm": sums[0] / k, "finalize": sums[1] / k, "update": sums[2] / k}
+    st = Z.neox_scaler_state(h)
+    grad[0:1].copy_(saved)
+    torch.cuda.synchronize()
+    done = 2 + steps + (steps if events else 0)
+    assert st.skipped_total - before == done and st.last_skipped == 1, "steps were not skipped"
+    return ms, kernels
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +334,8 @@ def main():
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--no-timing-events", action="store_true",
                     help="time whole steps only (no per-kernel events)")
+    ap.add_argument("--skip-steps", type=int, default=20,
+                    help="steps timed with an inf in the gradient after the applied ones (0: none)")
     ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
                     help="run only a plain streaming copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-pmc", action="store_true",
@@ -435,8 +470,14 @@ def main():
             one_step()
         sums, k2 = Z.neox_zero1_timing_end(h)
         kernel_ms = [sums[0] / k2, sums[1] / k2, update_ms]
-    Z.neox_zero1_destroy(h)
     assert st.skipped_total == 0 and st.step == args.warmup + args.steps, "bench steps were skipped"
+    skipped = None
+    if args.skip_steps > 0:
+        print(f"[bench] {args.skip_steps} skipped steps (inf in the gradient)", file=sys.stderr,
+              flush=True)
+        skipped = time_skipped_steps(Z, h, keep[0]["grad"], one_step, args.skip_steps,
+                                     timed_events)
+    Z.neox_zero1_destroy(h)
     ceiling = measure_ceiling(keep[0], n) if (w.flat and n % 8 == 0 and not sgd
                                              and not args.no_ceiling) else None
 
@@ -476,6 +517,12 @@ def main():
                            "bytes_per_launch": upd_bpp * n}
         out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],
                                 "update": kernel_ms[2]}
+    if skipped:
+        sk_ms, sk_kernels = skipped
+        out["skipped_step"] = {"steps": args.skip_steps, "ms_per_step": sk_ms,
+                               "bytes": 2 * n, "gbps": 2 * n / (sk_ms * 1e-3) / 1e9}
+        if sk_kernels:
+            out["skipped_step"]["kernel_avg_ms"] = sk_kernels
     if ceiling:
         ceiling["note"] = ("measured on this GPU right after the timed steps: a kernel with the "
                            "update's access pattern and trivial arithmetic, best of the launch "
