@@ -58,6 +58,12 @@ int hip_fail(hipError_t e, const char* what) {
 #ifndef NZ1_FLAT_BLOCKS_PER_CU_SGD
 #define NZ1_FLAT_BLOCKS_PER_CU_SGD 4
 #endif
+// Timing events skip the system-scope fence an event otherwise performs when it
+// completes (an L2 write-back and invalidate that slows the kernels after it): they are
+// only read for elapsed times, and every readback of results synchronizes by itself.
+#ifndef NZ1_TIMING_EVENT_FLAGS
+#define NZ1_TIMING_EVENT_FLAGS hipEventDisableSystemFence
+#endif
 constexpr uint32_t kDefaultChunk = NZ1_UPDATE_CHUNK;
 constexpr uint32_t kNormChunk = NZ1_NORM_CHUNK;
 
@@ -710,14 +716,19 @@ extern "C" int neox_zero1_destroy(neox_zero1* h) {
     return NEOX_OK;
 }
 
+static void clear_timing(neox_zero1* h) {
+    for (auto& s : h->timing)
+        for (auto& e : s.ev)
+            if (e) (void)hipEventDestroy(e);
+    h->timing.clear();
+    h->timing_used = 0;
+}
+
 extern "C" int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only) {
     if (!h || max_steps < 1 || max_steps > 1000000 || update_only < 0 || update_only > 1)
         return fail(NEOX_EINVAL, "bad timing request");
+    clear_timing(h);
     h->timing_update_only = update_only != 0;
-    for (auto& s : h->timing)
-        for (auto& e : s.ev) (void)hipEventDestroy(e);
-    h->timing.clear();
-    h->timing_used = 0;
     try {
         h->timing.resize(max_steps);
     } catch (const std::bad_alloc&) {
@@ -727,8 +738,11 @@ extern "C" int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t
         for (auto& e : s.ev) e = nullptr;
     for (auto& s : h->timing)
         for (auto& e : s.ev) {
-            hipError_t r = hipEventCreate(&e);
-            if (r != hipSuccess) return hip_fail(r, "hipEventCreate");
+            hipError_t r = hipEventCreateWithFlags(&e, NZ1_TIMING_EVENT_FLAGS);
+            if (r != hipSuccess) {
+                clear_timing(h);   // no half-made slots: later steps run untimed
+                return hip_fail(r, "hipEventCreate");
+            }
         }
     return NEOX_OK;
 }
@@ -748,10 +762,7 @@ extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* st
         }
     }
     *steps = h->timing_used;
-    for (auto& s : h->timing)
-        for (auto& e : s.ev) (void)hipEventDestroy(e);
-    h->timing.clear();
-    h->timing_used = 0;
+    clear_timing(h);
     return NEOX_OK;
 }
 

@@ -319,7 +319,7 @@ __device__ __forceinline__ double ipow(double b, int64_t t) {
 
 // The step's decisions from its squared norm (one thread): skip, clip coefficient, step
 // count, bias corrections and the loss-scale state machine, written to the state block.
-// The state is read once up front (one batch of scalar loads) and written at the end.
+// Each state field is read once, before the decision, and written at the end.
 __device__ __forceinline__ void finalize_state(double sumsq, DevState* __restrict__ st,
                                                const FinalizeArgs& a) {
     const float scale0 = st->loss_scale;
