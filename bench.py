@@ -13,6 +13,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,7 +26,12 @@ STEP_BYTES_PER_PARAM = 30        # + the norm pass's 2-byte gradient read
 # the sources that fix the kernels' code and launch shapes
 KERNEL_SRCS = tuple(os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
                     for f in ("zero1_kernels.hip", "zero1_internal.h", "zero1_api.hip"))
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "flat_update_kernel_neox20b_shard_215m_pmc.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def pmc_summary(workload, kernel):
+    """The committed counter summary of one update kernel on one workload."""
+    return os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
 
 
 def kernel_sha():
@@ -36,19 +42,23 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def read_traffic(workload, n):
-    """HBM bytes per update launch from the committed rocprofv3 PMC summary, scaled by
-    its copy-kernel calibration factor; None if absent or taken on other kernel code."""
-    if not os.path.exists(PMC_SUMMARY):
+def read_traffic(workload, n, kernel="flat_update_kernel"):
+    """HBM bytes per launch of the update kernel `kernel` from the committed rocprofv3 PMC
+    summary for this workload, scaled by its copy-kernel calibration factors; None if
+    there is none, or it was taken on other kernel code, workload or kernel."""
+    path = pmc_summary(workload, kernel)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     try:
         if vals.get("kernel_source_sha256") != kernel_sha() or vals.get("workload") != workload:
+            return None
+        if kernel not in re.findall(r"nz1::(\w+)<", vals.get("kernel", "")):
             return None
         return 1024.0 * (float(vals["fetch_kib_per_dispatch"]) * float(vals["copy_factor_fetch"])
                          + float(vals["write_kib_per_dispatch"]) * float(vals["copy_factor_write"]))
@@ -509,10 +519,11 @@ def main():
     if kernel_ms:
         upd_gbs = upd_bpp * n / (kernel_ms[2] * 1e-3) / 1e9
         default_mode = not (sgd or args.segment_norms)
+        upd_name = "flat_update_kernel" if flat_path else "update_kernel"
         out["roofline"] = {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": upd_gbs / HBM_PEAK_GBS,
-                           "traffic": read_traffic(w.name, n) if default_mode else None,
-                           "kernel": "flat_update_kernel" if flat_path else "update_kernel",
+                           "traffic": read_traffic(w.name, n, upd_name) if default_mode else None,
+                           "kernel": upd_name,
                            "avg_ms": kernel_ms[2],
                            "bytes_per_launch": upd_bpp * n}
         out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],

@@ -50,9 +50,20 @@ def test_pmc_summary_and_traffic_readback(tmp_path, monkeypatch, capsys):
     assert float(vals["copy_factor_fetch"]) == 2.0 and float(vals["copy_factor_write"]) == 1.0
     want = 1024.0 * (1001.0 * 2.0 + 3000.0 * 1.0)
     assert float(vals["traffic_bytes_per_dispatch"]) == round(want)
-    monkeypatch.setattr(bench, "PMC_SUMMARY", str(out))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    os.replace(out, bench.pmc_summary("neox20b_shard_215m", "flat_update_kernel"))
     assert bench.read_traffic("neox20b_shard_215m", N215) == want
-    assert bench.read_traffic("tiny_1m", 1 << 20) is None              # other workload
+    assert bench.read_traffic("tiny_1m", 1 << 20) is None              # no summary for it
+    # a summary filed under another workload's or kernel's name is not used
+    os.replace(bench.pmc_summary("neox20b_shard_215m", "flat_update_kernel"),
+               bench.pmc_summary("tiny_1m", "flat_update_kernel"))
+    assert bench.read_traffic("tiny_1m", 1 << 20) is None
+    os.replace(bench.pmc_summary("tiny_1m", "flat_update_kernel"),
+               bench.pmc_summary("neox20b_shard_215m", "update_kernel"))
+    assert bench.read_traffic("neox20b_shard_215m", N215, "update_kernel") is None
+    os.replace(bench.pmc_summary("neox20b_shard_215m", "update_kernel"),
+               bench.pmc_summary("neox20b_shard_215m", "flat_update_kernel"))
+    assert bench.read_traffic("neox20b_shard_215m", N215) == want
     monkeypatch.setattr(bench, "kernel_sha", lambda: "0" * 64)
     assert bench.read_traffic("neox20b_shard_215m", N215) is None      # other kernel sources
 
