@@ -86,8 +86,10 @@ def summarize_trace(args):
         "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py "
         f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline --skip-steps 0 > <log>",
-        f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} --bench-log <log>",
-        f"# Calls = 3 warm-up + {args.trace_steps} timed steps (update-kernel events only) + 20 steps",
+        f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} "
+        f"--trace-steps {args.trace_steps} --bench-log <log>",
+        f"# Calls = 3 warm-up + {args.trace_steps} timed steps (update-kernel events only) + "
+        f"{min(20, args.trace_steps)} steps",
         "# with events around every kernel; the torch kernels that draw the synthetic inputs and the",
         "# ceiling probes are left out.  Durations in ns.",
         f"kernel_source_sha256: {kernel_sha()}",
