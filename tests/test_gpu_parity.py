@@ -203,6 +203,33 @@ def test_parity_after_restored_step_count(t0):
         assert chk.ost.step == t0 + 3
 
 
+_DEGENERATE = {
+    "zero_grad": {},                                # gradient all zero: norm 0, only decay moves w
+    "betas_zero": dict(beta1=0.0, beta2=0.0),       # Adam reduces to g / (|g| + eps)
+    "eps_zero": dict(eps=0.0),
+    "lr_zero": {},                                  # w and half unchanged, m and v move
+    "no_decay": dict(weight_decay=0.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_DEGENERATE))
+def test_degenerate_hyperparameters(case):
+    """Settings at the edge of what the method admits, against the oracle, on a flat
+    shard and on separately allocated, misaligned arrays: clipping must not divide by a
+    zero norm, and the arithmetic must not special-case any of them."""
+    w = _custom(f"degenerate_{case}", [5000, 3, 2048, 777], [True, False, True, False],
+                **_DEGENERATE[case])
+    if case == "zero_grad":
+        w.grad_sigma = 0.0
+    lr = 0.0 if case == "lr_zero" else None
+    log(f"case degenerate {case}")
+    for shard in (DeviceShard(w, flat=True), DeviceShard(w, flat=False, misalign=(1, 2, 1, 3, 1))):
+        chk = run_sequence(w, 3, lr=lr, shard=shard, where=f" {case}")
+        assert chk.ost.skipped_total == 0 and chk.ost.step == 3
+        if case == "zero_grad":
+            assert chk.ost.last_sumsq == 0.0 and chk.ost.last_coef == 1.0
+
+
 def _path(w, shard, **over):
     h = Z.neox_zero1_create(lib_config(w, **over), shard.neox_segments(),
                             torch.cuda.current_stream().cuda_stream)
