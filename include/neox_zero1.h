@@ -248,10 +248,13 @@ int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg);
  * makes the next max_steps calls of neox_zero1_step time their kernels: each of the
  * three kernels, or (update_only = 1) the update kernel only, is launched with a pair of
  * HIP events that its own dispatch stamps with its start and end (no marker packets are
- * added to the stream).  neox_zero1_timing_end() waits, writes the summed kernel
- * durations in milliseconds of the norm pass, the finalize and the update to ms_sums[3]
- * (host; the first two are 0 with update_only), the number of recorded steps to *steps,
- * and stops recording.
+ * added to the stream).  The events skip the system-scope fence at completion: they
+ * give elapsed times only and order nothing.  neox_zero1_timing_end() waits, writes
+ * the summed kernel durations in milliseconds of the norm pass, the finalize and the
+ * update to ms_sums[3] (host; the first two are 0 with update_only), the number of
+ * recorded steps to *steps, and stops recording.  max_steps is 1 .. 1,000,000; a new
+ * begin discards an unfinished recording; if an event cannot be created, nothing is
+ * recorded and later steps run untimed.
  * Errors: NEOX_EINVAL, NEOX_ENOMEM, NEOX_EHIP. */
 int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only);
 int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);
