@@ -230,6 +230,43 @@ def test_degenerate_hyperparameters(case):
             assert chk.ost.last_sumsq == 0.0 and chk.ost.last_coef == 1.0
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_hyperparameters(seed):
+    """Seeded random draws of every hyper-parameter at once (betas, eps, weight decay,
+    clip threshold, lr, pre-divide factor and rank count, half format, scaler mode) on a
+    random segment layout, flat or separately allocated, three steps against the oracle."""
+    rng = np.random.default_rng(4000 + seed)
+    dtype = [W.F16, W.BF16][seed % 2]
+    nseg = int(rng.integers(1, 6))
+    sizes = [int(x) for x in rng.integers(1, 20_000, nseg)]
+    decays = [bool(x) for x in rng.integers(0, 2, nseg)]
+    f = float(2.0 ** rng.integers(0, 4))
+    D = int(2 ** rng.integers(0, 4))
+    hy = dict(beta1=float(rng.choice([0.0, 0.5, 0.9, 0.99])),
+              beta2=float(rng.choice([0.0, 0.9, 0.95, 0.999])),
+              eps=float(rng.choice([1e-8, 1e-6, 1e-3])),
+              weight_decay=float(rng.choice([0.0, 0.01, 0.1])),
+              clip_norm=float(rng.choice([0.0, 0.3, 1.0, 10.0])),
+              predivide_factor=f, dp_world_size=D)
+    sigma = float(rng.choice([1e-5, 1e-3, 1e-1]))
+    if dtype == W.F16:
+        # the largest scale at which 6 sigma of the stored gradient stays finite in fp16
+        # after up to three growths (no step may skip)
+        top = int(np.floor(np.log2(65504.0 / (6 * 8 * sigma * D / f))))
+        hy.update(scaler_mode=W.DYNAMIC, init_scale=float(2.0 ** max(0, min(16, top))),
+                  growth_interval=int(rng.integers(1, 4)))
+    w = _custom(f"random_hyper{seed}", sizes, decays, dtype, **hy)
+    w.grad_sigma = sigma
+    w.grad_mult = D / f              # the stored gradient is summed over D ranks, each / f
+    lr = float(rng.choice([1e-5, 6e-4, 1e-2]))
+    flat = bool(seed % 3)
+    mis = (0, 0, 0, 0, 0) if flat else tuple(int(x) for x in rng.integers(0, 4, 5))
+    log(f"case random hyper seed={seed} dtype={dtype} sizes={sizes} hyper={hy} lr={lr} flat={flat}")
+    chk = run_sequence(w, 3, lr=lr, shard=DeviceShard(w, flat=flat, misalign=mis),
+                       where=f" seed={seed}")
+    assert chk.ost.skipped_total == 0 and chk.ost.step == 3
+
+
 def _path(w, shard, **over):
     h = Z.neox_zero1_create(lib_config(w, **over), shard.neox_segments(),
                             torch.cuda.current_stream().cuda_stream)
