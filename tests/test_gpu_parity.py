@@ -267,6 +267,35 @@ def test_random_hyperparameters(seed):
     assert chk.ost.skipped_total == 0 and chk.ost.step == 3
 
 
+def test_zero1_wrapper_equals_raw_calls():
+    """The Python convenience class (create on the current stream, step, state, close)
+    produces bitwise the raw C-ABI calls' results; a closed handle refuses to step."""
+    w = _custom("wrapper", [12_345, 7, 4096], [True, False, True])
+    a, b = DeviceShard(w), DeviceShard(w)
+    a.init_()
+    b.init_()
+    log("case Zero1 wrapper")
+    opt = Z.Zero1(lib_config(w), a.neox_segments())
+    stream = torch.cuda.current_stream().cuda_stream
+    h = Z.neox_zero1_create(lib_config(w), b.neox_segments(), stream)
+    try:
+        for k in range(3):
+            a.grads_(k, opt.state().loss_scale)
+            b.grads_(k, Z.neox_scaler_state(h).loss_scale)
+            opt.step(lr=6e-4)
+            Z.neox_zero1_step(h, 6e-4, stream)
+        sa, sb = opt.state(), Z.neox_scaler_state(h)
+        assert (sa.step, sa.loss_scale, sa.last_sumsq) == (sb.step, sb.loss_scale, sb.last_sumsq)
+        oa, ob = _outputs(a), _outputs(b)
+        for k in oa:
+            assert torch.equal(oa[k], ob[k]), k
+    finally:
+        opt.close()
+        Z.neox_zero1_destroy(h)
+    with pytest.raises(Z.NeoxError):
+        opt.step(lr=6e-4)
+
+
 def _path(w, shard, **over):
     h = Z.neox_zero1_create(lib_config(w, **over), shard.neox_segments(),
                             torch.cuda.current_stream().cuda_stream)
