@@ -66,6 +66,12 @@ def read_traffic(workload, n, kernel="flat_update_kernel"):
         return None
 
 
+def bench_flags_arg(args):
+    """The --bench-flags argument as it appears in a summary's own command line."""
+    fl = getattr(args, "bench_flags", "")
+    return f" --bench-flags='{fl}'" if fl else ""
+
+
 def summarize_trace(args):
     """Write the kernel-time summary (profiles/...) from a rocprofv3 --kernel-trace --stats
     run of this program, with the algorithmic bandwidth of the step's kernels and, given
@@ -80,14 +86,16 @@ def summarize_trace(args):
     with open(files[0]) as fh:
         rows = [r for r in csv.DictReader(fh) if "nz1::" in r["Name"]]
     n = W.BENCH_WORKLOADS[args.workload]().numel
+    flags = f" {args.bench_flags}" if getattr(args, "bench_flags", "") else ""
     per_param = {"update_kernel": UPDATE_BYTES_PER_PARAM, "norm_kernel": 2}
     lines = [
         f"# rocprofv3 kernel trace of the ZeRO-1 step on {args.workload} ({n} params), MI355X (gfx950).",
         "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py "
-        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline --skip-steps 0 > <log>",
+        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline --skip-steps 0"
+        f"{flags} > <log>",
         f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} "
-        f"--trace-steps {args.trace_steps} --bench-log <log>",
+        f"--trace-steps {args.trace_steps} --bench-log <log>{bench_flags_arg(args)}",
         f"# Calls = 3 warm-up + {args.trace_steps} timed steps (update-kernel events only) + "
         f"{min(20, args.trace_steps)} steps",
         "# with events around every kernel; the torch kernels that draw the synthetic inputs and the",
@@ -157,18 +165,20 @@ def summarize_pmc(args):
     import workloads as W
     n = W.BENCH_WORKLOADS[args.workload]().numel
     traffic = (fetch * ff + write * fw) * 1024.0
+    flags = f" {args.bench_flags}" if getattr(args, "bench_flags", "") else ""
     lines = [
         f"# HBM traffic of the update on {args.workload} ({n} params), from rocprofv3 PMC.",
         "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- python3 bench.py "
-        f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events --skip-steps 0",
+        f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events --skip-steps 0"
+        f"{flags}",
         "#   rocprofv3 --pmc WRITE_SIZE -d <write_dir> ... (same program)",
         f"#   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch_dir> --output-format csv -- python3 bench.py "
         f"--copy-probe-only {args.copy_bytes}",
         "#   rocprofv3 --pmc WRITE_SIZE -d <copy_write_dir> ... (same program)",
         f"#   python3 bench.py --summarize-pmc --workload {args.workload} --copy-bytes "
         f"{args.copy_bytes} --pmc-fetch <fetch_dir> --pmc-write <write_dir> "
-        "--pmc-copy-fetch <copy_fetch_dir> --pmc-copy-write <copy_write_dir>",
+        f"--pmc-copy-fetch <copy_fetch_dir> --pmc-copy-write <copy_write_dir>{bench_flags_arg(args)}",
         "# The copy probe reads and writes copy_bytes once per dispatch; its counter readings",
         "# give the factors that turn counter KiB into bytes.  Counters count traffic leaving",
         "# the L2 (Infinity Cache hits included).",
@@ -356,6 +366,8 @@ def main():
                     help="write the kernel-time summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--trace-steps", type=int, default=20)
     ap.add_argument("--bench-log")
+    ap.add_argument("--bench-flags", default="",
+                    help="extra bench.py flags the profiled runs used (recorded in the summary)")
     ap.add_argument("--pmc-fetch")
     ap.add_argument("--pmc-write")
     ap.add_argument("--pmc-copy-fetch")
