@@ -8,8 +8,10 @@
  * the global L2 norm, decoupled weight decay, and the write-back of the half copy.
  *
  * Sources (web pages on GPT-NeoX and OPT training):
- *   [NeoX] "GPT-NeoX: how it opened the door to democratised 100B-scale training"
- *          (ainews.cool article), section 技术深度解析 (technical deep dive): with
+ *   [NeoX] "GPT-NeoX：如何为开源社区打开千亿级大模型训练的“民主化”之门"
+ *          (ainews.cool article; roughly "GPT-NeoX: how it opens the door to
+ *          democratised 100B-scale training for the open-source community"),
+ *          section 技术深度解析 (technical deep dive): with
  *          ZeRO stage 1 the Adam moments are split over the data-parallel GPUs and
  *          each device updates only the shard it owns; parallelism-strategy table:
  *          DP + ZeRO communicates by reduce-scatter / all-gather.

@@ -17,7 +17,8 @@
 // Sources: FP32 Adam state with FP16 weights and dynamic loss scaling [OPT: Open
 // Pre-trained Transformer Language Models, paper card, 计算设置]; pre-divide factor
 // and clipping at 1.0 / 0.3 [same card, 方法适配]; each rank updates only its shard
-// [GPT-NeoX democratisation article, 技术深度解析].  Formulas: Adam with bias
+// [GPT-NeoX article "GPT-NeoX：如何为开源社区打开千亿级大模型训练的“民主化”之门",
+// 技术深度解析].  Formulas: Adam with bias
 // correction (Kingma & Ba), decoupled decay (Loshchilov & Hutter), loss scaling
 // (Micikevicius et al. 2018).
 #include "zero1_internal.h"

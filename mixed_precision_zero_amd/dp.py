@@ -1,7 +1,8 @@
 """The caller-side exchange of the split step across data-parallel ranks.
 
 The clip coefficient and the skip decision need the squared gradient norm over every
-rank's shard [GPT-NeoX democratisation article, 技术深度解析: ZeRO stage 1 shards the
+rank's shard [GPT-NeoX article
+"GPT-NeoX：如何为开源社区打开千亿级大模型训练的“民主化”之门", 技术深度解析: ZeRO stage 1 shards the
 optimizer state over the data-parallel ranks].  Each rank runs
 `neox_zero1_step_local`, then `global_sumsq` all-gathers the ranks' fp64 values and adds
 them in rank order, so every rank holds the same bits and takes the same skip and clip

@@ -277,7 +277,8 @@ void orc_step(const orc_config* cfg, orc_scaler* st, float lr,
 /* Element-by-element: element e of the padded flat concat belongs to rank e / P and
  * to the tensor whose range contains it (or to the padding past the last tensor);
  * consecutive elements of one rank with the same owner form one segment.
- * [GPT-NeoX democratisation article, section "技术深度解析": each device updates only
+ * [GPT-NeoX article "GPT-NeoX：如何为开源社区打开千亿级大模型训练的“民主化”之门",
+ * section "技术深度解析": each device updates only
  * the shard it owns; parallelism table: DP + ZeRO uses reduce-scatter / all-gather.] */
 int64_t orc_partition(const uint64_t* tensor_numel, const uint8_t* tensor_decay,
                       int64_t ntensors, int64_t dp_world_size, int64_t rank, int64_t align,

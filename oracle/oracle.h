@@ -9,7 +9,8 @@
  * What it computes, and which passage of the pages it follows:
  *   - Each data-parallel rank updates only its own shard of the Adam state; the
  *     optimizer memory is divided by the DP degree.
- *       [GPT-NeoX democratisation article, section "技术深度解析" (technical deep dive),
+ *       [GPT-NeoX article "GPT-NeoX：如何为开源社区打开千亿级大模型训练的“民主化”之门"
+ *        (ainews.cool), section "技术深度解析" (technical deep dive),
  *        ZeRO stage-1 paragraph and the parallelism-strategy table]
  *   - Adam state kept in FP32, model weights kept in FP16, dynamic loss scaling.
  *       [OPT: Open Pre-trained Transformer Language Models (paper card),
