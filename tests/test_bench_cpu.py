@@ -108,3 +108,30 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_summaries_record_extra_bench_flags(tmp_path):
+    """A profile taken with extra bench flags (e.g. --chunked-update) states them in the
+    commands its header gives, so the summary names the run that reproduces it."""
+    args = _pmc_args(tmp_path, tmp_path / "s.txt")
+    args.bench_flags = "--chunked-update"
+    bench.summarize_pmc(args)
+    head = [ln for ln in (tmp_path / "s.txt").read_text().splitlines() if ln.startswith("#")]
+    assert any("--skip-steps 0 --chunked-update" in ln for ln in head)
+    assert any("--bench-flags='--chunked-update'" in ln for ln in head)
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "t_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
+                                          "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow(dict(Name="void nz1::update_kernel<1, 2, 0>(nz1::Chunk const*)", Calls=23,
+                        TotalDurationNs=23, AverageNs=1.0, Percentage=90, MinNs=1, MaxNs=1,
+                        StdDev=0))
+    out = tmp_path / "trace.txt"
+    bench.summarize_trace(argparse.Namespace(trace=str(d), workload="neox20b_shard_215m",
+                                             trace_steps=10, bench_log=None, out=str(out),
+                                             bench_flags="--chunked-update"))
+    text = out.read_text()
+    assert "--steps 10 --warmup 3 --no-cpu-baseline --skip-steps 0 --chunked-update" in text
+    assert "+ 10 steps" in text and "--trace-steps 10" in text
