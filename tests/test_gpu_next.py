@@ -57,6 +57,49 @@ def test_split_step_equals_step_on_one_rank():
         assert torch.equal(outs[0][k], outs[1][k]), k
 
 
+@pytest.mark.parametrize("optimizer", [Z.NEOX_OPT_ADAMW, Z.NEOX_OPT_SGD], ids=["adamw", "sgd"])
+def test_split_step_with_telemetry_and_sgd(optimizer):
+    """The split step combined with per-segment telemetry, for both optimizers: outputs,
+    scaler state and every segment's squared norm equal the fused step's bit for bit,
+    over clean steps and one with a NaN (whose segment alone reports a non-finite norm)."""
+    w = _custom("split_combo", [30_000, 2048, 17, 9000], [True, False, True, False],
+                clip_norm=0.05, optimizer=optimizer)
+    w.injections = {1: [(30_000 + 2048 + 5, "nan")]}       # element 5 of segment 2
+    stream = torch.cuda.current_stream().cuda_stream
+    results = []
+    for mode in ("step", "split"):
+        sh = DeviceShard(w)
+        sh.init_()
+        h = Z.neox_zero1_create(lib_config(w, segment_norms=1), sh.neox_segments(), stream)
+        loc = torch.zeros(1, dtype=torch.float64, device="cuda")
+        seq = []
+        try:
+            for k in range(4):
+                sh.grads_(k, Z.neox_scaler_state(h).loss_scale)
+                if mode == "step":
+                    Z.neox_zero1_step(h, 1e-3, stream)
+                else:
+                    Z.neox_zero1_step_local(h, loc.data_ptr(), stream)
+                    Z.neox_zero1_step_apply(h, loc.data_ptr(), 1e-3, stream)
+                st = Z.neox_scaler_state(h)
+                seg = Z.neox_zero1_segment_sumsq(h, len(w.segments))
+                seq.append(((st.loss_scale, st.step, st.skipped_total, st.last_sumsq),
+                            [float(x) for x in seg]))
+        finally:
+            Z.neox_zero1_destroy(h)
+        results.append((_outputs(sh), seq))
+        log(f"case split+telemetry optimizer={optimizer} mode={mode}")
+    (out_a, seq_a), (out_b, seq_b) = results
+    assert [s for s, _ in seq_a] == [s for s, _ in seq_b]
+    for (_, ga), (_, gb) in zip(seq_a, seq_b):
+        assert np.array_equal(np.array(ga), np.array(gb), equal_nan=True)
+    skipped = seq_a[1][1]
+    assert [bool(np.isfinite(x)) for x in skipped] == [True, True, False, True]
+    assert seq_a[1][0][2] == 1                                # that step was skipped
+    for k in out_a:
+        assert torch.equal(out_a[k], out_b[k]), k
+
+
 @pytest.mark.parametrize("D", [4, 8])
 def test_split_step_ranks_match_the_global_oracle(D):
     """D ZeRO-1 ranks of one model on this GPU, one after another: each runs step_local,
