@@ -6,7 +6,9 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SO = os.path.join(HERE, "liboracle.so")
+# NEOX_ORACLE_SO points the tests at another build of the same source (e.g. one with
+# host sanitizers); build_oracle(force=False) then uses it as it is.
+SO = os.environ.get("NEOX_ORACLE_SO", os.path.join(HERE, "liboracle.so"))
 
 # No fast-math and no FP contraction: every arithmetic line of the oracle is one IEEE
 # operation in the precision it names.
