@@ -6,8 +6,16 @@ unscale + clip + AdamW + cast update.  Inputs are synthetic and already resident
 HBM.  Prints one JSON line:
   value     params/s over the timed steps (wall clock between synchronizations)
   roofline  the update kernel (the dominant one): algorithmic bytes per launch over its
-            average duration from HIP events on its stream, against 8 TB/s
+            average duration from HIP events its own dispatch stamps, against 8 TB/s;
+            traffic = HBM bytes per launch from the committed rocprofv3 counter summary
+            of this workload and kernel (null when there is none for the current sources)
+  kernel_avg_ms  norm / finalize / update durations (a short all-kernel pass after)
+  skipped_step   the cost of a step with an inf in the gradient (timed last)
+  ceiling   a kernel with the update's access pattern and trivial arithmetic, swept over
+            launch shapes, and a plain copy, both on this GPU right after the timed steps
   cpu_baseline  the CPU oracle, single thread, on a bounded sample of the workload
+Other modes: --summarize-trace / --summarize-pmc write the profiles/ summaries from
+rocprofv3 output; --copy-probe-only is the counters' calibration copy.
 """
 import argparse
 import hashlib
