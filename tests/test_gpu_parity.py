@@ -233,8 +233,9 @@ def test_degenerate_hyperparameters(case):
 @pytest.mark.parametrize("seed", range(8))
 def test_random_hyperparameters(seed):
     """Seeded random draws of every hyper-parameter at once (betas, eps, weight decay,
-    clip threshold, lr, pre-divide factor and rank count, half format, scaler mode) on a
-    random segment layout, flat or separately allocated, three steps against the oracle."""
+    clip threshold, lr, pre-divide factor and rank count, half format, scaler mode,
+    optimizer) on a random segment layout, flat or separately allocated, three steps
+    against the oracle."""
     rng = np.random.default_rng(4000 + seed)
     dtype = [W.F16, W.BF16][seed % 2]
     nseg = int(rng.integers(1, 6))
@@ -261,7 +262,9 @@ def test_random_hyperparameters(seed):
     lr = float(rng.choice([1e-5, 6e-4, 1e-2]))
     flat = bool(seed % 3)
     mis = (0, 0, 0, 0, 0) if flat else tuple(int(x) for x in rng.integers(0, 4, 5))
-    log(f"case random hyper seed={seed} dtype={dtype} sizes={sizes} hyper={hy} lr={lr} flat={flat}")
+    w.hyper.optimizer = int(rng.integers(0, 2))      # AdamW or momentum SGD
+    log(f"case random hyper seed={seed} dtype={dtype} sizes={sizes} hyper={hy} lr={lr} "
+        f"flat={flat} optimizer={w.hyper.optimizer}")
     chk = run_sequence(w, 3, lr=lr, shard=DeviceShard(w, flat=flat, misalign=mis),
                        where=f" seed={seed}")
     assert chk.ost.skipped_total == 0 and chk.ost.step == 3
