@@ -334,3 +334,55 @@ def test_step_replayed_from_a_hip_graph_matches_eager():
         del g
         Z.neox_zero1_destroy(he)
         Z.neox_zero1_destroy(hg)
+
+
+# ----------------------------------------------------------------------------------
+# per-kernel timing (what the benchmark's roofline reads)
+# ----------------------------------------------------------------------------------
+
+def test_timing_events_record_and_change_nothing():
+    """Timed steps give the untimed steps' bits; all-kernel and update-only recordings
+    count the steps they cover (up to max_steps), report positive durations that fit in
+    the wall-clock time of those steps, and a new begin discards an unfinished one."""
+    import time
+    w = _custom("timing", [3_000_000, 7, 1_000_001], [True, False, True])
+    stream = torch.cuda.current_stream().cuda_stream
+    a, b = DeviceShard(w), DeviceShard(w)
+    a.init_()
+    b.init_()
+    ha = Z.neox_zero1_create(lib_config(w), a.neox_segments(), stream)
+    hb = Z.neox_zero1_create(lib_config(w), b.neox_segments(), stream)
+    log("case timing events")
+    try:
+        def both(k):
+            a.grads_(k, Z.neox_scaler_state(ha).loss_scale)
+            b.grads_(k, Z.neox_scaler_state(hb).loss_scale)
+            torch.cuda.synchronize()
+            Z.neox_zero1_step(ha, 1e-3, stream)
+            Z.neox_zero1_step(hb, 1e-3, stream)
+
+        Z.neox_zero1_timing_begin(ha, 3)                 # all three kernels
+        t0 = time.perf_counter()
+        for k in range(4):                               # the 4th step is not recorded
+            both(k)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        sums, n = Z.neox_zero1_timing_end(ha)
+        assert n == 3 and all(s > 0.0 for s in sums), (n, sums)
+        assert sum(sums) < wall_ms, (sums, wall_ms)
+        assert sums[2] > sums[1]                         # the update outlasts the finalize
+        Z.neox_zero1_timing_begin(ha, 5)                 # discarded by the next begin
+        both(4)
+        Z.neox_zero1_timing_begin(ha, 5, update_only=True)
+        for k in range(5, 7):
+            both(k)
+        sums, n = Z.neox_zero1_timing_end(ha)
+        assert n == 2 and sums[0] == 0.0 and sums[1] == 0.0 and sums[2] > 0.0, (n, sums)
+        sa, sb = Z.neox_scaler_state(ha), Z.neox_scaler_state(hb)
+        assert sa.step == sb.step == 7 and sa.last_sumsq == sb.last_sumsq
+        oa, ob = _outputs(a), _outputs(b)
+        for k in oa:
+            assert torch.equal(oa[k], ob[k]), k
+    finally:
+        Z.neox_zero1_destroy(ha)
+        Z.neox_zero1_destroy(hb)
