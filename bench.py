@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 UPDATE_BYTES_PER_PARAM = 28      # grad 2 + master/m/v 12 read; master/m/v 12 + half 2 written
+SGD_UPDATE_BYTES_PER_PARAM = 20  # momentum SGD keeps no second moment
 STEP_BYTES_PER_PARAM = 30        # + the norm pass's 2-byte gradient read
 # the sources that fix the kernels' code and launch shapes
 KERNEL_SRCS = tuple(os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
@@ -37,9 +38,20 @@ KERNEL_SRCS = tuple(os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def pmc_summary(workload, kernel):
+def pmc_summary(workload, kernel, optimizer="adamw"):
     """The committed counter summary of one update kernel on one workload."""
-    return os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
+    tag = "" if optimizer == "adamw" else f"_{optimizer}"
+    return os.path.join(PROFILES, f"{kernel}{tag}_{workload}_pmc.txt")
+
+
+def flags_optimizer(args):
+    """The optimizer a profiled run used, from the bench flags it recorded."""
+    fl = getattr(args, "bench_flags", "") or ""
+    return "sgd" if re.search(r"--optimizer[ =]sgd", fl) else "adamw"
+
+
+def update_bytes(optimizer):
+    return SGD_UPDATE_BYTES_PER_PARAM if optimizer == "sgd" else UPDATE_BYTES_PER_PARAM
 
 
 def kernel_sha():
@@ -50,11 +62,12 @@ def kernel_sha():
     return h.hexdigest()
 
 
-def read_traffic(workload, n, kernel="flat_update_kernel"):
+def read_traffic(workload, n, kernel="flat_update_kernel", optimizer="adamw"):
     """HBM bytes per launch of the update kernel `kernel` from the committed rocprofv3 PMC
-    summary for this workload, scaled by its copy-kernel calibration factors; None if
-    there is none, or it was taken on other kernel code, workload or kernel."""
-    path = pmc_summary(workload, kernel)
+    summary for this workload and optimizer, scaled by its copy-kernel calibration
+    factors; None if there is none, or it was taken on other kernel code, workload,
+    kernel or optimizer."""
+    path = pmc_summary(workload, kernel, optimizer)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -67,6 +80,8 @@ def read_traffic(workload, n, kernel="flat_update_kernel"):
         if vals.get("kernel_source_sha256") != kernel_sha() or vals.get("workload") != workload:
             return None
         if kernel not in re.findall(r"nz1::(\w+)<", vals.get("kernel", "")):
+            return None
+        if vals.get("optimizer", "adamw") != optimizer:
             return None
         return 1024.0 * (float(vals["fetch_kib_per_dispatch"]) * float(vals["copy_factor_fetch"])
                          + float(vals["write_kib_per_dispatch"]) * float(vals["copy_factor_write"]))
@@ -95,7 +110,7 @@ def summarize_trace(args):
         rows = [r for r in csv.DictReader(fh) if "nz1::" in r["Name"]]
     n = W.BENCH_WORKLOADS[args.workload]().numel
     flags = f" {args.bench_flags}" if getattr(args, "bench_flags", "") else ""
-    per_param = {"update_kernel": UPDATE_BYTES_PER_PARAM, "norm_kernel": 2}
+    per_param = {"update_kernel": update_bytes(flags_optimizer(args)), "norm_kernel": 2}
     lines = [
         f"# rocprofv3 kernel trace of the ZeRO-1 step on {args.workload} ({n} params), MI355X (gfx950).",
         "# Commands (from the repository root, on an MI355X):",
@@ -174,6 +189,8 @@ def summarize_pmc(args):
     n = W.BENCH_WORKLOADS[args.workload]().numel
     traffic = (fetch * ff + write * fw) * 1024.0
     flags = f" {args.bench_flags}" if getattr(args, "bench_flags", "") else ""
+    opt = flags_optimizer(args)
+    bpp = update_bytes(opt)
     lines = [
         f"# HBM traffic of the update on {args.workload} ({n} params), from rocprofv3 PMC.",
         "# Commands (from the repository root, on an MI355X):",
@@ -191,6 +208,7 @@ def summarize_pmc(args):
         "# give the factors that turn counter KiB into bytes.  Counters count traffic leaving",
         "# the L2 (Infinity Cache hits included).",
         f"workload: {args.workload}",
+        f"optimizer: {opt}",
         f"kernel: {', '.join(sorted(names))}",
         f"kernel_source_sha256: {kernel_sha()}",
         f"update_dispatches: {nf}",
@@ -202,8 +220,8 @@ def summarize_pmc(args):
         f"copy_factor_fetch: {ff:.5f}",
         f"copy_factor_write: {fw:.5f}",
         f"traffic_bytes_per_dispatch: {traffic:.0f}",
-        f"algorithmic_bytes_per_dispatch: {UPDATE_BYTES_PER_PARAM * n}",
-        f"traffic_over_algorithmic: {traffic / (UPDATE_BYTES_PER_PARAM * n):.4f}",
+        f"algorithmic_bytes_per_dispatch: {bpp * n}",
+        f"traffic_over_algorithmic: {traffic / (bpp * n):.4f}",
     ]
     text = "\n".join(lines) + "\n"
     if args.out:
@@ -408,7 +426,7 @@ def main():
     sgd = args.optimizer == "sgd"
     w.hyper.optimizer = 1 if sgd else 0
     n = w.numel
-    upd_bpp = 20 if sgd else UPDATE_BYTES_PER_PARAM     # SGD: no second moment to move
+    upd_bpp = update_bytes(args.optimizer)
     step_bpp = upd_bpp + 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -540,11 +558,12 @@ def main():
     }
     if kernel_ms:
         upd_gbs = upd_bpp * n / (kernel_ms[2] * 1e-3) / 1e9
-        default_mode = not (sgd or args.segment_norms)
+        default_mode = not args.segment_norms
         upd_name = "flat_update_kernel" if flat_path else "update_kernel"
         out["roofline"] = {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": upd_gbs / HBM_PEAK_GBS,
-                           "traffic": read_traffic(w.name, n, upd_name) if default_mode else None,
+                           "traffic": read_traffic(w.name, n, upd_name, args.optimizer)
+                           if default_mode else None,
                            "kernel": upd_name,
                            "avg_ms": kernel_ms[2],
                            "bytes_per_launch": upd_bpp * n}

@@ -135,3 +135,26 @@ def test_summaries_record_extra_bench_flags(tmp_path):
     text = out.read_text()
     assert "--steps 10 --warmup 3 --no-cpu-baseline --skip-steps 0 --chunked-update" in text
     assert "+ 10 steps" in text and "--trace-steps 10" in text
+
+
+def test_sgd_summary_is_kept_apart(tmp_path, monkeypatch):
+    """A counter summary of the momentum-SGD step (20 B/param, its own file name) is read
+    for SGD runs only, and an AdamW summary never serves an SGD run."""
+    args = _pmc_args(tmp_path, tmp_path / "s.txt")
+    args.bench_flags = "--optimizer sgd"
+    bench.summarize_pmc(args)
+    vals = dict(line.split(": ", 1) for line in (tmp_path / "s.txt").read_text().splitlines()
+                if ": " in line and not line.startswith("#"))
+    assert vals["optimizer"] == "sgd" and vals["algorithmic_bytes_per_dispatch"] == str(20 * N215)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    sgd_path = bench.pmc_summary("neox20b_shard_215m", "flat_update_kernel", "sgd")
+    assert sgd_path.endswith("flat_update_kernel_sgd_neox20b_shard_215m_pmc.txt")
+    os.replace(tmp_path / "s.txt", sgd_path)
+    want = 1024.0 * (1001.0 * 2.0 + 3000.0 * 1.0)
+    assert bench.read_traffic("neox20b_shard_215m", N215, "flat_update_kernel", "sgd") == want
+    assert bench.read_traffic("neox20b_shard_215m", N215, "flat_update_kernel") is None
+    # an AdamW summary filed under the SGD name is refused
+    args.bench_flags = ""
+    bench.summarize_pmc(args)
+    os.replace(tmp_path / "s.txt", sgd_path)
+    assert bench.read_traffic("neox20b_shard_215m", N215, "flat_update_kernel", "sgd") is None
