@@ -30,7 +30,10 @@ int neox_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t nt_store
  * 256 or 512), `vectors` 8-element vectors per thread (1, 2 or 4; a tile is threads x
  * vectors x 8 elements), at most `blocks_per_cu` blocks per CU (0 = as many as fit;
  * 1..16, enforced by reserving LDS), stores non-temporal when nt_stores != 0.  The
- * arrays' contents are changed. */
+ * arrays' contents are changed.  Unlike the update, a thread may start storing its
+ * first vector before the loads of its later vectors return; at 2 or 4 vectors per
+ * thread that ordering makes the pattern slower than the update at the same shape, so
+ * the ceiling is the best shape, not a fixed one. */
 int neox_probe_update_pattern(const void* grad, void* half, float* master, float* exp_avg,
                               float* exp_avg_sq, uint64_t n, int32_t threads, int32_t vectors,
                               int32_t blocks_per_cu, int32_t nt_stores, void* hip_stream);
