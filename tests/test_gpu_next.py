@@ -267,6 +267,34 @@ def test_segment_norms_match_oracle():
         chk.close()
 
 
+@pytest.mark.parametrize("flat", [True, False], ids=["flat", "separate"])
+def test_segment_norms_many_segments(flat):
+    """2,000 segments of 1 .. 3,000 elements (many norm blocks, tiny segments): every
+    segment's squared norm matches the oracle's scan of that segment, and they add up to
+    the step's squared norm."""
+    rng = np.random.default_rng(2000 + flat)
+    sizes = [int(x) for x in rng.integers(1, 3001, 2000)]
+    decays = [bool(x) for x in rng.integers(0, 2, 2000)]
+    w = _custom("telemetry_many", sizes, decays)
+    sh = DeviceShard(w, flat=flat)
+    sh.init_()
+    chk = Checker(sh, segment_norms=1)
+    log(f"case telemetry 2000 segments flat={flat} n={sum(sizes)}")
+    try:
+        sh.grads_(0, chk.scale())
+        inv, inv32 = O.unscale_factor(chk.ocfg, chk.ost)
+        want = [O.scan(W.F16, sh.host_window(i, 0, n)["grad"], inv, inv32)[0]
+                for i, n in enumerate(sizes)]
+        chk.step(6e-4, check=False, where=" telemetry many")
+        got = Z.neox_zero1_segment_sumsq(chk.handle, len(sizes))
+        st = Z.neox_scaler_state(chk.handle)
+        for i, (g, ws) in enumerate(zip(got, want)):
+            assert abs(g - ws) <= 1e-5 * ws + 1e-300, (i, g, ws)
+        assert abs(sum(got) - st.last_sumsq) <= 1e-12 * st.last_sumsq
+    finally:
+        chk.close()
+
+
 # ----------------------------------------------------------------------------------
 # momentum SGD
 # ----------------------------------------------------------------------------------
