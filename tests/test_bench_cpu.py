@@ -158,3 +158,45 @@ def test_sgd_summary_is_kept_apart(tmp_path, monkeypatch):
     bench.summarize_pmc(args)
     os.replace(tmp_path / "s.txt", sgd_path)
     assert bench.read_traffic("neox20b_shard_215m", N215, "flat_update_kernel", "sgd") is None
+
+
+def test_skipped_step_timing_restores_the_gradient(monkeypatch):
+    """bench.time_skipped_steps plants an inf at gradient element 0, runs the skipped steps
+    (two untimed, K timed, K with events), restores the element, and refuses a run in
+    which the steps were not skipped.  A fake library stands in for the GPU here."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+    grad = torch.full((16,), 3.0, dtype=torch.float16)
+
+    class FakeState:
+        def __init__(self, skipped, last):
+            self.skipped_total, self.last_skipped = skipped, last
+
+    class FakeLib:
+        def __init__(self, skips):
+            self.skips, self.skipped, self.events = skips, 0, None
+
+        def neox_scaler_state(self, h):
+            return FakeState(self.skipped, 1 if self.skipped else 0)
+
+        def neox_zero1_timing_begin(self, h, k):
+            self.events = k
+
+        def neox_zero1_timing_end(self, h):
+            return [0.06 * self.events, 0.004 * self.events, 0.02 * self.events], self.events
+
+    def make_step(lib):
+        def step():
+            assert torch.isinf(grad[0]) and grad[1] == 3.0      # the inf is in place
+            if lib.skips:
+                lib.skipped += 1
+        return step
+
+    lib = FakeLib(skips=True)
+    ms, kernels = bench.time_skipped_steps(lib, 0, grad, make_step(lib), 5, events=True)
+    assert lib.skipped == 2 + 5 + 5 and ms >= 0.0
+    assert kernels == pytest.approx({"norm": 0.06, "finalize": 0.004, "update": 0.02})
+    assert torch.equal(grad, torch.full((16,), 3.0, dtype=torch.float16))   # restored
+    lib = FakeLib(skips=False)
+    with pytest.raises(AssertionError):
+        bench.time_skipped_steps(lib, 0, grad, make_step(lib), 3, events=False)
