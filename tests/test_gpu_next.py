@@ -326,13 +326,17 @@ def test_sgd_parity(dtype, misalign):
 # graph capture
 # ----------------------------------------------------------------------------------
 
-def test_step_replayed_from_a_hip_graph_matches_eager():
+@pytest.mark.parametrize("mode", ["adamw", "sgd", "split"])
+def test_step_replayed_from_a_hip_graph_matches_eager(mode):
     """The step enqueues only kernels (no allocation, no memset, no host sync), so a
-    caller can capture it in a HIP graph.  Replays, with eager gradient generation and
-    synchronisations between them and an overflow on one step, match the eager step bit
-    for bit every time."""
-    w = _custom("graph", [200_000, 777, 65_536], [True, False, True], clip_norm=0.01)
+    caller can capture it in a HIP graph: the whole step, the momentum-SGD step, or the
+    split step's two halves around a device double.  Replays, with eager gradient
+    generation and synchronisations between them and an overflow on one step, match the
+    eager step bit for bit every time."""
+    w = _custom("graph", [200_000, 777, 65_536], [True, False, True], clip_norm=0.01,
+                optimizer=1 if mode == "sgd" else 0)
     w.injections = {3: [(1234, "+inf")]}
+    log(f"case graph {mode}")
     eager, graphed = DeviceShard(w), DeviceShard(w)
     eager.init_()
     graphed.init_()
@@ -341,9 +345,15 @@ def test_step_replayed_from_a_hip_graph_matches_eager():
     side = torch.cuda.Stream()
     hg = Z.neox_zero1_create(lib_config(w), graphed.neox_segments(), side.cuda_stream)
     g = torch.cuda.CUDAGraph()
+    loc = torch.zeros(1, dtype=torch.float64, device="cuda")      # allocated before capture
     try:
         with torch.cuda.graph(g, stream=side):
-            Z.neox_zero1_step(hg, 1e-3, torch.cuda.current_stream().cuda_stream)
+            cap = torch.cuda.current_stream().cuda_stream
+            if mode == "split":
+                Z.neox_zero1_step_local(hg, loc.data_ptr(), cap)
+                Z.neox_zero1_step_apply(hg, loc.data_ptr(), 1e-3, cap)
+            else:
+                Z.neox_zero1_step(hg, 1e-3, cap)
         torch.cuda.synchronize()
         for k in range(6):
             eager.grads_(k, Z.neox_scaler_state(he).loss_scale)
