@@ -230,6 +230,94 @@ def summarize_pmc(args):
     print(text, end="")
 
 
+# per pass: at most 4 TCC, 4 TCP and 2 GRBM counters (one hardware pass each)
+STALL_PASSES = (
+    "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_STALL_sum GRBM_GUI_ACTIVE",
+    "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_LEVEL_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_sum",
+    "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_WRITE_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_TCC_WRITE_REQ_sum",
+    "TCC_BUSY_sum TCC_TAG_STALL_sum TCP_PENDING_STALL_CYCLES_sum GRBM_GUI_ACTIVE",
+    "TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum TCC_HIT_sum TCC_MISS_sum",
+)
+# gfx950: 8 XCDs of 16 L2 channels each
+L2_CHANNELS = 128
+
+
+def _kernel_key(name):
+    return name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+
+
+def summarize_stalls(args):
+    """The memory-side counter table of the step's kernels next to the copy and access-
+    pattern probes, from the rocprofv3 --pmc runs of STALL_PASSES (one sub-directory per
+    pass under args.stalls): duration, effective shader clock, L2-to-memory request
+    counts, latencies and requests in flight, credit stalls."""
+    import csv
+    import glob
+    rows = {}
+    durs = {}
+    nxcc = 8
+    for f in sorted(glob.glob(os.path.join(args.stalls, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                k = _kernel_key(r["Kernel_Name"])
+                if not (k.startswith("nz1::") or "copy_kernel<" in k and "at::" not in k
+                        or k.startswith("pattern_kernel")):
+                    continue
+                rows.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for f in glob.glob(os.path.join(args.stalls, "**", "*agent_info.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Agent_Type") == "GPU":
+                    nxcc = int(r["Num_Xcc"])
+    if not rows:
+        raise SystemExit(f"no step or probe kernels in counter files under {args.stalls}")
+    lines = [
+        "# Memory-side counters of the step's kernels and of the bandwidth probes, MI355X (gfx950).",
+        "# Commands (from the repository root, on an MI355X), one run per counter pass:",
+    ]
+    for i, ps in enumerate(STALL_PASSES):
+        lines.append(f"#   rocprofv3 --pmc {ps} -d <dir>/p{i + 1} --output-format csv -- python3 bench.py "
+                     f"--workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline "
+                     f"--no-timing-events --skip-steps 0 --no-extra-workloads")
+    lines += [
+        f"#   python3 bench.py --summarize-stalls <dir> --workload {args.workload}",
+        "# Per dispatch (averages).  cycles = GRBM_GUI_ACTIVE / XCDs; clock = cycles / duration.",
+        "# rd/wr req: L2-to-memory requests (TCC_EA0_*REQ_sum); B/req = algorithmic bytes / requests",
+        "# (update kernels only).  lat = LEVEL_sum / REQ_sum (cycles a request waits for memory);",
+        "# inflight = LEVEL_sum / cycles (chip-wide requests outstanding, x B/req = bytes in flight).",
+        f"# stall% = credit-stall channel-cycles / (cycles x {L2_CHANNELS} L2 channels).",
+        "# tcp_rd_lat = TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum (CU to L2 round trip).",
+        f"kernel_source_sha256: {kernel_sha()}",
+        f"{'kernel':34s} {'n':>4s} {'us':>8s} {'GHz':>6s} {'rd_req':>9s} {'wr_req':>9s} "
+        f"{'rd_lat':>7s} {'rd_infl':>8s} {'wr_lat':>7s} {'wr_infl':>8s} {'rdstl%':>7s} {'wrstl%':>7s} "
+        f"{'tcp_rd_lat':>10s} {'L2hit%':>7s}",
+    ]
+    def a(c, k):
+        v = c.get(k)
+        return sum(v) / len(v) if v else float("nan")
+    for k in sorted(rows, key=lambda x: (not x.startswith("nz1::"), x)):
+        c = rows[k]
+        cyc = a(c, "GRBM_GUI_ACTIVE") / nxcc
+        us = sum(durs[k]) / len(durs[k]) / 1e3 if k in durs else float("nan")
+        rd, wr = a(c, "TCC_EA0_RDREQ_sum"), a(c, "TCC_EA0_WRREQ_sum")
+        rl, wl = a(c, "TCC_EA0_RDREQ_LEVEL_sum"), a(c, "TCC_EA0_WRREQ_LEVEL_sum")
+        hit, miss = a(c, "TCC_HIT_sum"), a(c, "TCC_MISS_sum")
+        lines.append(
+            f"{k[:34]:34s} {len(durs.get(k, [])):4d} {us:8.1f} {cyc / (us * 1e3):6.3f} {rd:9.0f} {wr:9.0f} "
+            f"{rl / rd:7.0f} {rl / cyc:8.0f} {wl / wr:7.0f} {wl / cyc:8.0f} "
+            f"{100 * a(c, 'TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum') / (cyc * L2_CHANNELS):7.2f} "
+            f"{100 * a(c, 'TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum') / (cyc * L2_CHANNELS):7.2f} "
+            f"{a(c, 'TCP_TCC_READ_REQ_LATENCY_sum') / a(c, 'TCP_TCC_READ_REQ_sum'):10.0f} "
+            f"{100 * hit / (hit + miss):7.1f}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text, end="")
+
+
 def copy_probe(nbytes):
     """A plain streaming copy of known size for counter calibration: reads and writes
     nbytes once per dispatch, three dispatches."""
@@ -287,21 +375,46 @@ def measure_ceiling(bufs, n, reps=20):
             "copy_gbps": copy}
 
 
-def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
-    """The oracle as it stands, one thread, on the first `sample` params of the shard."""
-    import numpy as np
+def host_info():
+    """The host the CPU baseline ran on: logical CPUs, the ones this process may use, the
+    CPU model and the RAM."""
+    info = {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": None, "ram_gb": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    info["ram_gb"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    return info
 
+
+# the box's CPU share for one GPU: at most this many oracle threads
+CPU_THREADS_MAX = 16
+
+
+def _oracle_setup(w, n=None):
+    """Host inputs of workload w (its first n params) for the oracle: config, scaler and
+    the segment list over freshly drawn arrays (the step-0 gradient)."""
     import workloads as W
     from oracle import oracle as O
 
-    sample = min(sample, w.numel)
-    segs, left = [], sample
-    for n, d in w.segments:
+    n = w.numel if n is None else min(n, w.numel)
+    segs, left = [], n
+    for k, d in w.segments:
         if left == 0:
             break
-        segs.append((min(n, left), d))
+        segs.append((min(k, left), d))
         left -= segs[-1][0]
-    st0 = W.host_init(w, n=sample)
+    st0 = W.host_init(w, n=n)
+    g = W.host_grads(w, 0, w.hyper.init_scale, n=n)
     h = w.hyper
     cfg = O.Config(beta1=h.beta1, beta2=h.beta2, eps=h.eps, weight_decay=h.weight_decay,
                    clip_norm=h.clip_norm, predivide_factor=h.predivide_factor,
@@ -309,23 +422,67 @@ def cpu_baseline(w, budget_s=12.0, sample=1 << 24):
                    growth_interval=h.growth_interval, growth_factor=h.growth_factor,
                    backoff_factor=h.backoff_factor, min_scale=h.min_scale,
                    optimizer=h.optimizer)
-    st = O.Scaler(loss_scale=h.init_scale)
+    osegs, off = [], 0
+    for k, d in segs:
+        sl = slice(off, off + k)
+        osegs.append(dict(grad=g[sl], half=st0["half"][sl], master=st0["master"][sl],
+                          m=st0["m"][sl], v=None if h.optimizer else st0["v"][sl], decay=d))
+        off += k
+    return cfg, O.Scaler(loss_scale=h.init_scale), osegs, n
+
+
+def _time_oracle(cfg, st, segs, n, threads, budget_s, max_steps):
+    """Steps of the oracle as it stands (one thread: its own whole-step routine; more:
+    its routines over static contiguous pieces, partials added in thread order) until
+    the budget is spent; returns (params/s, steps, seconds)."""
+    import numpy as np
+
+    from oracle import oracle as O
+    lr = np.float32(6e-4)
     spent, steps = 0.0, 0
-    while spent < budget_s and steps < 50:
-        g = W.host_grads(w, steps, st.loss_scale, n=sample)
-        osegs, off = [], 0
-        for n, d in segs:
-            sl = slice(off, off + n)
-            osegs.append(dict(grad=g[sl], half=st0["half"][sl], master=st0["master"][sl],
-                              m=st0["m"][sl], v=None if h.optimizer else st0["v"][sl], decay=d))
-            off += n
+    while steps < 1 or (spent < budget_s and steps < max_steps):
         t0 = time.perf_counter()
-        O.step(cfg, st, np.float32(h.lr), osegs)
+        if threads == 1:
+            O.step(cfg, st, lr, segs)
+        else:
+            O.step_parallel(cfg, st, lr, segs, threads)
         spent += time.perf_counter() - t0
         steps += 1
-    return {"value": sample * steps / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {sample} params of the shard ({len(segs)} segments), {steps} steps, "
-                      f"{spent:.1f} s of single-thread oracle time (fp64 scalar C, -O2)"}
+    return n * steps / spent, steps, spent
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The CPU oracle on this host: the bench workload in full, on all the cores this
+    process may use (up to the box's share) and on one thread, plus the two small
+    workloads on all cores.  Same seeded inputs as the GPU side (host draws)."""
+    import workloads as W
+
+    info = host_info()
+    threads = max(1, min(CPU_THREADS_MAX, info["affinity_cpus"]))
+    cfg, st, segs, n = _oracle_setup(w)
+    rate_t, steps_t, sec_t = _time_oracle(cfg, st, segs, n, threads, budget_s / 2, 20)
+    # the same arrays, carried on: every step does the same work whatever their values
+    rate_1, steps_1, sec_1 = _time_oracle(cfg, st, segs, n, 1, budget_s, 3)
+    del segs
+    small = {}
+    for name, mk in (("tiny_1m", W.tiny), ("pythia410m_dp8_rank0", lambda: W.pythia410m(0))):
+        sw = mk()
+        c, s2, sg, k = _oracle_setup(sw)
+        r, ns, sec = _time_oracle(c, s2, sg, k, threads, 1.0, 20)
+        small[name] = {"value": r, "params": k, "steps": ns, "seconds": round(sec, 2),
+                       "cores": threads}
+    what = (f"{w.name} in full ({n} params, {len(w.segments)} segments), step-0 gradient; "
+            f"all-core: {steps_t} steps on {threads} threads in {sec_t:.1f} s (static contiguous "
+            f"pieces, per-thread double partial sums added in thread order); one thread: "
+            f"{steps_1} steps in {sec_1:.1f} s; fp64 scalar C, gcc -O2")
+    return {"value": rate_t, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": what,
+            "gbps": STEP_BYTES_PER_PARAM * rate_t / 1e9,
+            "single_thread": {"value": rate_1, "cores": 1, "steps": steps_1,
+                              "seconds": round(sec_1, 2),
+                              "gbps": STEP_BYTES_PER_PARAM * rate_1 / 1e9},
+            "other_workloads_in_full": small,
+            "host": info}
 
 
 def time_skipped_steps(Z, h, grad, one_step, steps, events):
@@ -361,85 +518,21 @@ def time_skipped_steps(Z, h, grad, one_step, steps, events):
     return ms, kernels
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="neox20b_shard_215m")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the attainable-bandwidth probes after the timed steps")
-    ap.add_argument("--optimizer", choices=("adamw", "sgd"), default="adamw",
-                    help="sgd: momentum SGD on the same shard (no second moment)")
-    ap.add_argument("--split", action="store_true",
-                    help="time the split step (step_local + step_apply on the local value)")
-    ap.add_argument("--segment-norms", action="store_true",
-                    help="keep per-segment squared norms (telemetry) during the step")
-    ap.add_argument("--chunked-update", action="store_true",
-                    help="run the update from the per-chunk work table even on a flat shard")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph and time its replays")
-    ap.add_argument("--no-timing-events", action="store_true",
-                    help="time whole steps only (no per-kernel events)")
-    ap.add_argument("--skip-steps", type=int, default=20,
-                    help="steps timed with an inf in the gradient after the applied ones (0: none)")
-    ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
-                    help="run only a plain streaming copy of BYTES (counter calibration)")
-    ap.add_argument("--summarize-pmc", action="store_true",
-                    help="write the update kernel's traffic summary from rocprofv3 --pmc runs")
-    ap.add_argument("--summarize-trace", metavar="DIR", dest="trace",
-                    help="write the kernel-time summary of a rocprofv3 --kernel-trace --stats run")
-    ap.add_argument("--trace-steps", type=int, default=20)
-    ap.add_argument("--bench-log")
-    ap.add_argument("--bench-flags", default="",
-                    help="extra bench.py flags the profiled runs used (recorded in the summary)")
-    ap.add_argument("--pmc-fetch")
-    ap.add_argument("--pmc-write")
-    ap.add_argument("--pmc-copy-fetch")
-    ap.add_argument("--pmc-copy-write")
-    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
-    ap.add_argument("--out")
-    args = ap.parse_args()
-    if args.summarize_pmc:
-        summarize_pmc(args)
-        return
-    if args.trace:
-        summarize_trace(args)
-        return
-    if args.copy_probe_only:
-        copy_probe(args.copy_probe_only)
-        return
-    if args.gpus != 1:
-        print(f"bench.py: the step is one rank's work and is measured on one GPU only "
-              f"(--gpus {args.gpus} requested); multi-GPU runs are not supported", file=sys.stderr)
-        sys.exit(2)
-
+def alloc_shard(w, dev, sgd):
+    """The workload's five device arrays (one buffer per array for a flat shard, else one
+    allocation per array per segment), initialized, with the step-0 gradient drawn; the
+    segment list for the library.  Returns (buffer dicts, segments)."""
     import torch
 
     import mixed_precision_zero_amd as Z
     import workloads as W
-
-    if args.workload not in W.BENCH_WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; one of {sorted(W.BENCH_WORKLOADS)}")
-    w = W.BENCH_WORKLOADS[args.workload]()
-    sgd = args.optimizer == "sgd"
-    w.hyper.optimizer = 1 if sgd else 0
-    n = w.numel
-    upd_bpp = update_bytes(args.optimizer)
-    step_bpp = upd_bpp + 2
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     dt = torch.float16 if w.hyper.dtype == W.F16 else torch.bfloat16
-    print(f"[bench] workload {w.name}: {n} params, {len(w.segments)} segments, "
-          f"{'flat' if w.flat else 'separate allocations'}", file=sys.stderr, flush=True)
-
-    keep = []
-    segs = []
     kinds = [("grad", dt), ("half", dt), ("master", torch.float32), ("m", torch.float32)]
     if not sgd:
         kinds.append(("v", torch.float32))
+    keep, segs = [], []
     if w.flat:
+        n = w.numel
         bufs = {k: torch.empty(n, dtype=t, device=dev) for k, t in kinds}
         bufs.setdefault("v", None)
         W.device_init_(w, bufs["master"], bufs["half"], bufs["m"], bufs["v"])
@@ -462,16 +555,197 @@ def main():
             segs.append(Z.segment(a["grad"], a["half"], a["master"], a["m"], a["v"], decay))
             keep.append(a)
             off += numel
-    stream = torch.cuda.current_stream()
-    h = Z.neox_zero1_create(Z.neox_zero1_default_config(
+    return keep, segs
+
+
+def lib_config(Z, w, **over):
+    return Z.neox_zero1_default_config(
         beta1=w.hyper.beta1, beta2=w.hyper.beta2, eps=w.hyper.eps,
         weight_decay=w.hyper.weight_decay, clip_norm=w.hyper.clip_norm,
         predivide_factor=w.hyper.predivide_factor, dp_world_size=w.hyper.dp_world_size,
         dtype=w.hyper.dtype, scaler_mode=w.hyper.scaler_mode,
         growth_interval=w.hyper.growth_interval, init_scale=w.hyper.init_scale,
-        min_scale=w.hyper.min_scale, optimizer=w.hyper.optimizer,
-        segment_norms=int(args.segment_norms), chunked_update=int(args.chunked_update)),
-        segs, stream.cuda_stream)
+        min_scale=w.hyper.min_scale, optimizer=w.hyper.optimizer, **over)
+
+
+def median(xs):
+    ys = sorted(xs)
+    k = len(ys)
+    return ys[k // 2] if k % 2 else 0.5 * (ys[k // 2 - 1] + ys[k // 2])
+
+
+def timed_steps(Z, h, one_step, steps, events):
+    """K steps by wall clock between synchronizations (the update kernel's own dispatch
+    events recording on the side when `events`), then, with events, K more steps with all
+    three kernels timed for the per-step durations (norm start to update end) and the
+    norm / finalize split.  Returns a dict of the timings in ms."""
+    import torch
+    if events:
+        Z.neox_zero1_timing_begin(h, steps, update_only=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    out = {"wall_ms": (t1 - t0) * 1e3 / steps}
+    if events:
+        sums, k, upd = Z.neox_zero1_timing_end(h, per_step=steps)
+        out["update_ms"] = sums[2] / k
+        out["update_median_ms"], out["update_min_ms"] = median(upd), min(upd)
+        Z.neox_zero1_timing_begin(h, steps)
+        for _ in range(steps):
+            one_step()
+        sums, k, per = Z.neox_zero1_timing_end(h, per_step=steps)
+        out["norm_ms"], out["finalize_ms"] = sums[0] / k, sums[1] / k
+        out["step_median_ms"], out["step_min_ms"] = median(per), min(per)
+        out["event_steps"] = k
+    return out
+
+
+def extra_workload(name, dev, steps, warmup):
+    """One more workload end to end (allocate, create, warm up, time, free): its line of
+    the `workloads` object."""
+    import gc
+
+    import torch
+
+    import mixed_precision_zero_amd as Z
+    import workloads as W
+    w = W.BENCH_WORKLOADS[name]()
+    n = w.numel
+    print(f"[bench] workload {name}: {n} params, {len(w.segments)} segments", file=sys.stderr,
+          flush=True)
+    keep, segs = alloc_shard(w, dev, sgd=False)
+    stream = torch.cuda.current_stream()
+    h = Z.neox_zero1_create(lib_config(Z, w), segs, stream.cuda_stream)
+    try:
+        flat_path = Z.neox_zero1_update_path(h) == Z.NEOX_PATH_FLAT
+
+        def one_step():
+            Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
+
+        for _ in range(warmup):
+            one_step()
+        t = timed_steps(Z, h, one_step, steps, events=True)
+        st = Z.neox_scaler_state(h)
+        assert st.skipped_total == 0 and st.step == warmup + 2 * steps, "bench steps were skipped"
+    finally:
+        Z.neox_zero1_destroy(h)
+        del keep, segs
+        gc.collect()
+        torch.cuda.empty_cache()
+    upd_gbs = UPDATE_BYTES_PER_PARAM * n / (t["update_ms"] * 1e-3) / 1e9
+    return {"params": n, "segments": len(w.segments),
+            "layout": "flat shard" if w.flat else "separate allocations",
+            "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
+            "update_path": "flat" if flat_path else "chunked",
+            "steps": steps, "warmup": warmup,
+            "value": n / (t["wall_ms"] * 1e-3), "unit": "params/s",
+            "ms_per_step": t["wall_ms"], "ms_per_step_median": t["step_median_ms"],
+            "ms_per_step_min": t["step_min_ms"],
+            "step_gbps": STEP_BYTES_PER_PARAM * n / (t["wall_ms"] * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "kernel": "flat_update_kernel" if flat_path else "update_kernel",
+                         "achieved": upd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": upd_gbs / HBM_PEAK_GBS, "avg_ms": t["update_ms"],
+                         "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
+            "kernel_avg_ms": {"norm": t["norm_ms"], "finalize": t["finalize_ms"],
+                              "update": t["update_ms"]}}
+
+
+# the other shards of at least 2e8 params, timed in the default run: the largest one that
+# fits one GPU (OPT-style, 6e9 params, 96 GB of state) and the 5,000 separately allocated
+# tensors (chunk-table update)
+EXTRA_WORKLOADS = (("opt_style_6b", 6, 2), ("multi_tensor_5000_bf16", 20, 3))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="neox20b_shard_215m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the copy / access-pattern probes after the timed steps")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="time only --workload (not the other >= 2e8-param shards)")
+    ap.add_argument("--optimizer", choices=("adamw", "sgd"), default="adamw",
+                    help="sgd: momentum SGD on the same shard (no second moment)")
+    ap.add_argument("--split", action="store_true",
+                    help="time the split step (step_local + step_apply on the local value)")
+    ap.add_argument("--segment-norms", action="store_true",
+                    help="keep per-segment squared norms (telemetry) during the step")
+    ap.add_argument("--chunked-update", action="store_true",
+                    help="run the update from the per-chunk work table even on a flat shard")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
+    ap.add_argument("--no-timing-events", action="store_true",
+                    help="time whole steps only (no per-kernel events)")
+    ap.add_argument("--skip-steps", type=int, default=20,
+                    help="steps timed with an inf in the gradient after the applied ones (0: none)")
+    ap.add_argument("--copy-probe-only", type=int, default=0, metavar="BYTES",
+                    help="run only a plain streaming copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-pmc", action="store_true",
+                    help="write the update kernel's traffic summary from rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-trace", metavar="DIR", dest="trace",
+                    help="write the kernel-time summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-stalls", metavar="DIR", dest="stalls",
+                    help="write the memory-side counter table (update against copy) from rocprofv3 "
+                         "--pmc runs under DIR")
+    ap.add_argument("--trace-steps", type=int, default=20)
+    ap.add_argument("--bench-log")
+    ap.add_argument("--bench-flags", default="",
+                    help="extra bench.py flags the profiled runs used (recorded in the summary)")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--pmc-copy-fetch")
+    ap.add_argument("--pmc-copy-write")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--out")
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.trace:
+        summarize_trace(args)
+        return
+    if args.stalls:
+        summarize_stalls(args)
+        return
+    if args.copy_probe_only:
+        copy_probe(args.copy_probe_only)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: the step is one rank's work and is measured on one GPU only "
+              f"(--gpus {args.gpus} requested); multi-GPU runs are not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import gc
+
+    import torch
+
+    import mixed_precision_zero_amd as Z
+    import workloads as W
+
+    if args.workload not in W.BENCH_WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; one of {sorted(W.BENCH_WORKLOADS)}")
+    w = W.BENCH_WORKLOADS[args.workload]()
+    sgd = args.optimizer == "sgd"
+    w.hyper.optimizer = 1 if sgd else 0
+    n = w.numel
+    upd_bpp = update_bytes(args.optimizer)
+    step_bpp = upd_bpp + 2
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {w.name}: {n} params, {len(w.segments)} segments, "
+          f"{'flat' if w.flat else 'separate allocations'}", file=sys.stderr, flush=True)
+
+    keep, segs = alloc_shard(w, dev, sgd)
+    stream = torch.cuda.current_stream()
+    h = Z.neox_zero1_create(lib_config(Z, w, segment_norms=int(args.segment_norms),
+                                       chunked_update=int(args.chunked_update)),
+                            segs, stream.cuda_stream)
     flat_path = Z.neox_zero1_update_path(h) == Z.NEOX_PATH_FLAT
     loc = torch.zeros(1, dtype=torch.float64, device=dev)
 
@@ -498,29 +772,13 @@ def main():
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
           flush=True)
 
-    # The timed steps record only the update kernel's two events; the norm / finalize
-    # split comes from a short pass with all events after the timed region.
+    # The timed steps record only the update kernel's two events; per-step durations and
+    # the norm / finalize split come from as many steps with all events right after.
     timed_events = not args.no_timing_events and not args.split and not args.graph
-    if timed_events:
-        Z.neox_zero1_timing_begin(h, args.steps, update_only=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    t = timed_steps(Z, h, one_step, args.steps, timed_events)
     st = Z.neox_scaler_state(h)
-    kernel_ms = None
-    if timed_events:
-        sums, k = Z.neox_zero1_timing_end(h)
-        update_ms = sums[2] / k
-        nb = min(20, args.steps)
-        Z.neox_zero1_timing_begin(h, nb)
-        for _ in range(nb):
-            one_step()
-        sums, k2 = Z.neox_zero1_timing_end(h)
-        kernel_ms = [sums[0] / k2, sums[1] / k2, update_ms]
-    assert st.skipped_total == 0 and st.step == args.warmup + args.steps, "bench steps were skipped"
+    done = args.warmup + args.steps * (2 if timed_events else 1)
+    assert st.skipped_total == 0 and st.step == done, "bench steps were skipped"
     skipped = None
     if args.skip_steps > 0:
         print(f"[bench] {args.skip_steps} skipped steps (inf in the gradient)", file=sys.stderr,
@@ -530,8 +788,11 @@ def main():
     Z.neox_zero1_destroy(h)
     ceiling = measure_ceiling(keep[0], n) if (w.flat and n % 8 == 0 and not sgd
                                              and not args.no_ceiling) else None
+    del keep, segs
+    gc.collect()
+    torch.cuda.empty_cache()
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = t["wall_ms"]
     value = n / (ms_per_step * 1e-3)
     out = {
         "metric": "params/sec per fused ZeRO-1 Adam step; achieved HBM GB/s vs MI355X peak",
@@ -541,6 +802,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": t.get("step_median_ms"),
+        "ms_per_step_min": t.get("step_min_ms"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -555,9 +818,13 @@ def main():
         "hbm": {"step_bytes": step_bpp * n,
                 "step_gbps": step_bpp * n / (ms_per_step * 1e-3) / 1e9,
                 "step_frac_of_peak": step_bpp * n / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "step_timing": {"value_and_ms_per_step": "wall clock over the timed steps",
+                        "median_and_min": "per-step durations from the kernels' own dispatch "
+                                          "events (norm start to update end), as many steps "
+                                          "right after the timed ones"},
     }
-    if kernel_ms:
-        upd_gbs = upd_bpp * n / (kernel_ms[2] * 1e-3) / 1e9
+    if timed_events:
+        upd_gbs = upd_bpp * n / (t["update_ms"] * 1e-3) / 1e9
         default_mode = not args.segment_norms
         upd_name = "flat_update_kernel" if flat_path else "update_kernel"
         out["roofline"] = {"bound": "hbm", "achieved": upd_gbs, "peak": HBM_PEAK_GBS,
@@ -565,10 +832,12 @@ def main():
                            "traffic": read_traffic(w.name, n, upd_name, args.optimizer)
                            if default_mode else None,
                            "kernel": upd_name,
-                           "avg_ms": kernel_ms[2],
+                           "avg_ms": t["update_ms"],
+                           "median_ms": t["update_median_ms"],
+                           "min_ms": t["update_min_ms"],
                            "bytes_per_launch": upd_bpp * n}
-        out["kernel_avg_ms"] = {"norm": kernel_ms[0], "finalize": kernel_ms[1],
-                                "update": kernel_ms[2]}
+        out["kernel_avg_ms"] = {"norm": t["norm_ms"], "finalize": t["finalize_ms"],
+                                "update": t["update_ms"]}
     if skipped:
         sk_ms, sk_kernels = skipped
         out["skipped_step"] = {"steps": args.skip_steps, "ms_per_step": sk_ms,
@@ -576,18 +845,28 @@ def main():
         if sk_kernels:
             out["skipped_step"]["kernel_avg_ms"] = sk_kernels
     if ceiling:
-        ceiling["note"] = ("measured on this GPU right after the timed steps: a kernel with the "
-                           "update's access pattern and trivial arithmetic, best of the launch "
-                           "shapes swept (threads x vectors per thread / blocks per CU / "
-                           "non-temporal stores), and a plain copy (best of plain and "
-                           "non-temporal stores)")
-        if kernel_ms:
-            ceiling["update_kernel_frac_of_pattern"] = out["roofline"]["achieved"] / \
+        ceiling["note"] = ("measured on this GPU right after the timed steps, on the same "
+                           "arrays: a plain copy (best of plain and non-temporal stores), the "
+                           "attainable rate of the simplest in-place-free stream; and a second "
+                           "kernel with the update's access pattern and trivial arithmetic, "
+                           "best of the launch shapes swept (threads x vectors per thread / "
+                           "blocks per CU / non-temporal stores) -- a comparison, not an upper "
+                           "bound")
+        if timed_events:
+            out["roofline"]["copy_gbps"] = ceiling["copy_gbps"]
+            out["roofline"]["frac_of_copy"] = out["roofline"]["achieved"] / ceiling["copy_gbps"]
+            ceiling["update_kernel_over_pattern"] = out["roofline"]["achieved"] / \
                 ceiling["update_pattern_gbps"]
-        ceiling["step_frac_of_pattern"] = out["hbm"]["step_gbps"] / ceiling["update_pattern_gbps"]
-        out["ceiling"] = ceiling
+        ceiling["step_over_copy"] = out["hbm"]["step_gbps"] / ceiling["copy_gbps"]
+        out["probes"] = ceiling
+    if not args.no_extra_workloads and not args.split and not args.graph and not sgd \
+            and not args.segment_norms and not args.chunked_update:
+        out["workloads"] = {}
+        for name, k, wu in EXTRA_WORKLOADS:
+            if name != w.name:
+                out["workloads"][name] = extra_workload(name, dev, k, wu)
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle, one thread)", file=sys.stderr, flush=True)
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

@@ -75,7 +75,9 @@ extern "C" {
  * floor 1.0). */
 typedef struct neox_zero1_config {
     double  beta1, beta2;          /* in [0, 1)                                         */
-    double  eps;                   /* >= 0, added to sqrt(v_hat)                        */
+    double  eps;                   /* > 0 (also after rounding to FP32), added to
+                                      sqrt(v_hat); 0 would make a zero gradient with zero
+                                      moments compute 0/0                               */
     double  weight_decay;          /* >= 0, decoupled: w -= lr * wd * w (DECAY segments) */
     double  clip_norm;             /* > 0: clip to this global L2 norm; <= 0: no clip   */
     double  predivide_factor;      /* f > 0: each rank divided its gradient by f        */
@@ -185,18 +187,26 @@ int neox_zero1_partition(const uint64_t* tensor_numel, const uint8_t* tensor_dec
                          uint32_t align, neox_shard_segment* out, uint64_t cap,
                          uint64_t* nseg_out, uint64_t* shard_numel_out);
 
-/* Create a step handle for one shard.  cfg and segs[nseg] are host memory, copied
+/* Create a step handle for one data-parallel rank's shard of the optimizer state: the
+ * rank keeps and updates only its own piece of the FP32 master weights and Adam moments
+ * [NeoX, 技术深度解析: ZeRO stage 1], which the OPT card keeps in FP32 next to FP16
+ * weights [OPT, 计算设置], 16 bytes per parameter in all [OPT, 瓶颈].
+ * cfg and segs[nseg] are host memory, copied
  * (the caller may free them on return).  The caller keeps ownership of every device
  * array; they must stay valid, and not be written by anyone else while a step runs,
  * until neox_zero1_destroy().  The library allocates its own device scratch (work
  * table, per-block partial sums, a state block) and uploads it on hip_stream, then
  * synchronizes that stream.  *out receives the handle.
  * Errors: NEOX_EINVAL (null pointers, nseg == 0, a zero-length or misaligned segment,
- * a config field out of the ranges above), NEOX_ENOMEM, NEOX_EHIP. */
+ * written arrays that overlap one another, a gradient that overlaps a written array, a
+ * config field out of the ranges above), NEOX_ENOMEM, NEOX_EHIP. */
 int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg,
                       void* hip_stream, neox_zero1** out);
 
-/* Enqueue one step on hip_stream and return without waiting: a norm/overflow pass
+/* One optimizer step with dynamic loss scaling [OPT, 计算设置]: skip on an inf/NaN
+ * gradient and back off the scale, the pre-divide factor folded into the unscale, and
+ * clipping by the global L2 norm (1.0, later 0.3 in the OPT run) [OPT, 方法适配].
+ * Enqueue it on hip_stream and return without waiting: a norm/overflow pass
  * over every gradient, a one-block finalize (skip decision, clip coefficient, step
  * count, bias corrections, loss-scale update, all on the device), and the fused
  * unscale + clip + AdamW + cast update, which returns before loading its data when the
@@ -206,12 +216,17 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
 int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream);
 
-/* Wait for the stream of the last call that enqueued work on this handle and copy the
+/* The loss scaler's state: the scale, its clean-step and overflow counters (a climbing
+ * overflow count at the floor is the scale collapse the OPT card describes [OPT, 瓶颈]),
+ * the step count and the last step's norm and clip coefficient.
+ * Wait for the stream of the last call that enqueued work on this handle and copy the
  * state to *out.  A step replayed from a captured HIP graph is not such a call: wait for
  * the replay's stream before reading the state.  Errors: NEOX_EINVAL (null), NEOX_EHIP. */
 int neox_scaler_state(neox_zero1* h, neox_scaler_state_t* out);
 
-/* Wait for outstanding work and free the library's scratch (never caller memory).
+/* End of a shard's optimizer (the caller keeps the FP32 state it owns [NeoX,
+ * 技术深度解析]).  Wait for outstanding work and free the library's scratch (never caller
+ * memory).
  * A graph that captured a step of this handle must not be replayed afterwards.
  * NULL is a no-op returning NEOX_OK. */
 int neox_zero1_destroy(neox_zero1* h);
@@ -222,14 +237,20 @@ int neox_zero1_destroy(neox_zero1* h);
  *   neox_zero1_step_local  enqueues the norm pass and writes this rank's squared norm
  *                          of the unscaled gradient to the device double *local_sumsq
  *                          (non-finite if any of its unscaled values overflowed);
- *   (caller)               sums the D ranks' values, in rank order so every rank gets
- *                          the same bits, into a device double on each rank;
- *   neox_zero1_step_apply  enqueues the finalize on *global_sumsq and the update.
- * neox_zero1_step is step_local followed by step_apply on the local value.  Both
- * return without waiting.  Errors: NEOX_EINVAL (null handle or pointer, pointer not
- * 8-byte aligned, non-finite lr), NEOX_EHIP. */
+ *   (caller)               gathers the D ranks' values, in rank order, into a device
+ *                          array rank_sumsq[D] on every rank (an all-gather: data
+ *                          movement only);
+ *   neox_zero1_step_apply  enqueues the finalize -- which adds rank_sumsq[0 .. nranks) in
+ *                          a fixed order, so every rank gets the same bits and takes the
+ *                          same skip and clip decisions; a non-finite value from any rank
+ *                          skips the step everywhere -- and the update.
+ * neox_zero1_step is step_local followed by step_apply on the local value alone
+ * (nranks = 1), bit for bit.  Both return without waiting.  Errors: NEOX_EINVAL (null
+ * handle or pointer, pointer not 8-byte aligned, nranks 0 or above 2^24, non-finite lr),
+ * NEOX_EHIP. */
 int neox_zero1_step_local(neox_zero1* h, double* local_sumsq, void* hip_stream);
-int neox_zero1_step_apply(neox_zero1* h, const double* global_sumsq, float lr, void* hip_stream);
+int neox_zero1_step_apply(neox_zero1* h, const double* rank_sumsq, uint32_t nranks, float lr,
+                          void* hip_stream);
 
 /* Overwrite the persistent scaler state in stream order: loss_scale, good_steps, step,
  * skipped_total and consecutive_overflows of *st (host) replace the device copy; the
@@ -254,12 +275,16 @@ int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg);
  * give elapsed times only and order nothing.  neox_zero1_timing_end() waits, writes
  * the summed kernel durations in milliseconds of the norm pass, the finalize and the
  * update to ms_sums[3] (host; the first two are 0 with update_only), the number of
- * recorded steps to *steps, and stops recording.  max_steps is 1 .. 1,000,000; a new
- * begin discards an unfinished recording; if an event cannot be created, nothing is
- * recorded and later steps run untimed.
- * Errors: NEOX_EINVAL, NEOX_ENOMEM, NEOX_EHIP. */
+ * recorded steps to *steps, and, when step_cap > 0, each of the first step_cap recorded
+ * steps' duration to the host array step_ms (from the norm pass's start to the update's
+ * end, launch gaps included; the update kernel alone with update_only), then stops
+ * recording.  max_steps is 1 .. 1,000,000; a new begin discards an unfinished recording;
+ * if an event cannot be created, nothing is recorded and later steps run untimed.
+ * Errors: NEOX_EINVAL (null handle or outputs, step_cap < 0, step_ms NULL with
+ * step_cap > 0), NEOX_ENOMEM, NEOX_EHIP. */
 int neox_zero1_timing_begin(neox_zero1* h, int32_t max_steps, int32_t update_only);
-int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps);
+int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* steps, double* step_ms,
+                          int64_t step_cap);
 
 /* Which update kernel the handle runs: NEOX_PATH_FLAT or NEOX_PATH_CHUNKED (see
  * chunked_update).  Errors: NEOX_EINVAL (null handle). */

@@ -106,11 +106,13 @@ def lib():
         L.neox_scaler_state.argtypes = [C.c_void_p, P(neox_scaler_state_t)]
         L.neox_zero1_destroy.argtypes = [C.c_void_p]
         L.neox_zero1_step_local.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
-        L.neox_zero1_step_apply.argtypes = [C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]
+        L.neox_zero1_step_apply.argtypes = [C.c_void_p, C.c_void_p, C.c_uint32, C.c_float,
+                                            C.c_void_p]
         L.neox_scaler_set.argtypes = [C.c_void_p, P(neox_scaler_state_t), C.c_void_p]
         L.neox_zero1_segment_sumsq.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64]
         L.neox_zero1_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
-        L.neox_zero1_timing_end.argtypes = [C.c_void_p, P(C.c_double), P(C.c_int64)]
+        L.neox_zero1_timing_end.argtypes = [C.c_void_p, P(C.c_double), P(C.c_int64),
+                                            P(C.c_double), C.c_int64]
         L.neox_zero1_update_path.argtypes = [C.c_void_p]
         L.neox_zero1_plan.argtypes = [P(neox_zero1_config), P(neox_segment), C.c_uint64,
                                       P(neox_zero1_plan_t), P(neox_chunk_info), C.c_uint64,
@@ -191,10 +193,12 @@ def neox_zero1_step_local(h: int, local_sumsq_ptr: int, stream_ptr: int = 0):
                                        C.c_void_p(stream_ptr)))
 
 
-def neox_zero1_step_apply(h: int, global_sumsq_ptr: int, lr: float, stream_ptr: int = 0):
-    """Finalize on the device double at global_sumsq_ptr, then the update."""
-    _check(lib().neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(global_sumsq_ptr), C.c_float(lr),
-                                       C.c_void_p(stream_ptr)))
+def neox_zero1_step_apply(h: int, rank_sumsq_ptr: int, lr: float, stream_ptr: int = 0,
+                          nranks: int = 1):
+    """Finalize on the fixed-order sum of the nranks device doubles at rank_sumsq_ptr (the
+    ranks' squared norms, in rank order), then the update."""
+    _check(lib().neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(rank_sumsq_ptr), nranks,
+                                       C.c_float(lr), C.c_void_p(stream_ptr)))
 
 
 def neox_scaler_set(h: int, loss_scale: float, good_steps=0, step=0, skipped_total=0,
@@ -244,11 +248,15 @@ def neox_zero1_plan(cfg: neox_zero1_config, segs, tables: bool = True):
     return plan, list(chunks[:plan.update_chunks]), list(words[:nw]), list(changes[:plan.flat_changes])
 
 
-def neox_zero1_timing_end(h: int):
-    """-> ([norm_ms, finalize_ms, update_ms] summed, steps)."""
+def neox_zero1_timing_end(h: int, per_step: int = 0):
+    """-> ([norm_ms, finalize_ms, update_ms] summed, steps); with per_step = K > 0 also
+    the durations (ms) of the first K recorded steps."""
     ms = (C.c_double * 3)()
     n = C.c_int64()
-    _check(lib().neox_zero1_timing_end(C.c_void_p(h), ms, C.byref(n)))
+    steps = (C.c_double * per_step)() if per_step > 0 else None
+    _check(lib().neox_zero1_timing_end(C.c_void_p(h), ms, C.byref(n), steps, max(0, per_step)))
+    if per_step > 0:
+        return list(ms), n.value, list(steps[:min(n.value, per_step)])
     return list(ms), n.value
 
 

@@ -110,9 +110,10 @@ struct KernelTiming {
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
                        const DevState* st, double* partial, uint32_t lds_reserve,
                        hipStream_t stream, const KernelTiming& t = {});
-hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
-                           DevState* st, const FinalizeArgs& a, hipStream_t stream,
-                           const KernelTiming& t = {});
+// The finalize sums partial[0, nparts) in a fixed order (the norm pass's partials, or the
+// ranks' squared norms of a split step), then takes the step's decisions.
+hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
+                           const FinalizeArgs& a, hipStream_t stream, const KernelTiming& t = {});
 hipError_t launch_reduce(const double* partial, uint32_t nparts, double* out, hipStream_t stream);
 hipError_t launch_segment_sumsq(const double* partial, const uint32_t* range, uint32_t nseg,
                                 double* out, hipStream_t stream);
@@ -126,10 +127,57 @@ hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const
                               const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream,
                               const KernelTiming& t = {});
 
+// Static LDS (bytes) of the norm kernel: launch reservations subtract it so that the
+// requested number of blocks per CU really fits.
+hipError_t norm_static_lds(uint32_t* bytes);
+
 // The unscale factor for scale s, computed in double and rounded once to FP32; the
 // host (initial state) and the finalize kernel evaluate the same expression.
 __host__ __device__ inline float unscale_factor(double predivide, double dp, float s) {
     return (float)(predivide / (dp * (double)s));
 }
+
+}  // namespace nz1
+
+// ------------------------------------------------------------------------------------
+// Host side shared by the C-ABI translation units (zero1_api.hip, zero1_noalloc.hip).
+// ------------------------------------------------------------------------------------
+#include "neox_zero1.h"
+
+#include <vector>
+
+namespace nz1 {
+
+// Records the message for neox_zero1_last_error() on this thread and returns code.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int set_hip_error(hipError_t e, const char* what);
+
+// The work decomposition of a segment list: what create() uploads and neox_zero1_plan()
+// describes.
+struct Plan {
+    uint32_t C = 0;                        // update chunk length
+    uint32_t C1 = 0;                       // norm chunk length
+    std::vector<Chunk> table, norm_table;  // update and norm work tables
+    bool flat = false;                     // flat partition: the update runs over tiles
+    uint64_t numel = 0;
+    std::vector<uint32_t> tile_word, change;
+};
+// Validates the config and the segments, then builds the tables.  NEOX_OK or an error
+// code (the message recorded).
+int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg, Plan& p);
+
+// Launch constants derived from a validated config.
+FinalizeArgs finalize_args(const neox_zero1_config& cfg);
+UpdateArgs update_args(const neox_zero1_config& cfg);   // lr left at 0
+// The device state block before the first step of a run: scaler counters as given,
+// unscale factor for `scale`, no decision yet (skip set).
+DevState initial_state(const neox_zero1_config& cfg, float scale, int32_t good_steps,
+                       int64_t step, int64_t skipped, int32_t consecutive);
+
+// Dynamic LDS each pass's blocks reserve (only to cap blocks per CU) on one device.
+struct LdsReserve {
+    uint32_t norm = 0, update = 0, flat = 0;
+};
+int lds_reserve(int device, int optimizer, LdsReserve* out);
 
 }  // namespace nz1

@@ -373,13 +373,13 @@ __device__ __forceinline__ void finalize_state(double sumsq, DevState* __restric
     st->inv = unscale_factor(a.predivide_factor, a.dp_world_size, scale);
 }
 
+// The squared norm is the fixed-order sum of nparts values: this handle's per-block
+// partials, or the data-parallel ranks' squared norms (the same order on every rank).
 __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* __restrict__ partial,
                                                                   uint32_t nparts,
-                                                                  const double* __restrict__ sumsq_in,
                                                                   DevState* __restrict__ st,
                                                                   FinalizeArgs a) {
-    // the squared norm: this handle's own partials, or a value summed over the ranks
-    const double sumsq = sumsq_in ? *sumsq_in : sum_partials(partial, nparts);
+    const double sumsq = sum_partials(partial, nparts);
     if (threadIdx.x == 0) finalize_state(sumsq, st, a);
 }
 
@@ -762,11 +762,9 @@ hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const double* partial, uint32_t nparts, const double* sumsq_in,
-                           DevState* st, const FinalizeArgs& a, hipStream_t stream,
-                           const KernelTiming& t) {
-    launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), 0, stream, t, partial, nparts, sumsq_in,
-           st, a);
+hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
+                           const FinalizeArgs& a, hipStream_t stream, const KernelTiming& t) {
+    launch(finalize_kernel, dim3(1), dim3(kFinalizeBlock), 0, stream, t, partial, nparts, st, a);
     return hipGetLastError();
 }
 
@@ -812,6 +810,13 @@ hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const
     else
         launch_flat_opt<0>(dtype, f, st, a, lds_reserve, stream, t);
     return hipGetLastError();
+}
+
+hipError_t norm_static_lds(uint32_t* bytes) {
+    hipFuncAttributes a{};
+    const hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&norm_kernel<1>));
+    *bytes = e == hipSuccess ? (uint32_t)a.sharedSizeBytes : 0u;
+    return e;
 }
 
 // lds_reserve: dynamic LDS the kernel never touches, requested only to cap how many

@@ -240,6 +240,67 @@ def step(cfg: Config, st: Scaler, lr, segments):
     return st
 
 
+def pieces(sizes, parts):
+    """Cut the concatenation of segments of the given sizes into `parts` contiguous pieces
+    of nearly equal length: per piece, the list of (segment, lo, hi) runs it covers."""
+    total = int(sum(sizes))
+    bounds = [total * p // parts for p in range(parts + 1)]
+    out, starts, off = [], [], 0
+    for n in sizes:
+        starts.append(off)
+        off += int(n)
+    for p in range(parts):
+        a, b, runs = bounds[p], bounds[p + 1], []
+        for k, n in enumerate(sizes):
+            lo, hi = max(a, starts[k]), min(b, starts[k] + int(n))
+            if lo < hi:
+                runs.append((k, lo - starts[k], hi - starts[k]))
+        out.append(runs)
+    return out
+
+
+def step_parallel(cfg: Config, st: Scaler, lr, segments, threads):
+    """One whole step with the elementwise work on `threads` host threads: the segments'
+    elements, concatenated, are cut into `threads` contiguous pieces; each thread scans
+    its piece into its own double partial sum (orc_scan), the partials are added in
+    thread order, one orc_decide takes the step's decisions, and each thread updates its
+    piece (orc_update / orc_update_sgd).  ctypes releases the interpreter lock during each
+    call, so the threads run in parallel.  Equals step() except for the summation order
+    of the squared norm (its last bits).  segments as for step()."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    sizes = [s["grad"].size for s in segments]
+    work = pieces(sizes, max(1, int(threads)))
+    inv, inv32 = unscale_factor(cfg, st)
+
+    def scan_piece(runs):
+        acc, of = 0.0, 0
+        for k, lo, hi in runs:
+            acc, of = scan(cfg.dtype, segments[k]["grad"][lo:hi], inv, inv32, acc, of)
+        return acc, of
+
+    def update_piece(d, runs):
+        for k, lo, hi in runs:
+            s = segments[k]
+            sl = slice(lo, hi)
+            if cfg.optimizer == SGD:
+                update_sgd(cfg, d, lr, s["grad"][sl], s["half"][sl], s["master"][sl],
+                           s["m"][sl], s.get("decay", False))
+            else:
+                update(cfg, d, lr, s["grad"][sl], s["half"][sl], s["master"][sl], s["m"][sl],
+                       s["v"][sl], s.get("decay", False))
+
+    with ThreadPoolExecutor(max_workers=len(work)) as ex:
+        parts = list(ex.map(scan_piece, work))
+        sumsq, of = 0.0, 0
+        for acc, o in parts:                  # thread order
+            sumsq += acc
+            of |= o
+        d = decide(cfg, st, of, sumsq)
+        list(ex.map(lambda runs: update_piece(d, runs), work))
+    return st
+
+
 def partition(tensor_numel, tensor_decay, dp_world_size, rank, align=64):
     """Segments of `rank` as a list of dicts, plus the shard length P."""
     numel = np.ascontiguousarray(tensor_numel, dtype=np.uint64)

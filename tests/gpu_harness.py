@@ -260,14 +260,15 @@ class Checker:
                              "own norm (pass overflow=None)")
         if not check:
             return gst, d
-        for i, lo, hi, p in pre:
-            post = sh.host_window(i, lo, hi)
+        posts = [sh.host_window(i, lo, hi) for i, lo, hi, _ in pre]
+
+        def compare(i, lo, hi, p, post):
             tag = f"{where} seg {i} [{lo}:{hi})"
             if d.skip:
                 for k in ("half", "master", "m", "v"):
                     if p[k] is not None:
                         assert np.array_equal(post[k], p[k]), f"{k}{tag} changed on a skipped step"
-                continue
+                return
             o = {k: (None if p[k] is None else p[k].copy()) for k in ARRAYS}
             if sh.sgd:
                 sm, sw = O.update_sgd(self.ocfg, d, np.float32(lr), o["grad"], o["half"],
@@ -284,4 +285,23 @@ class Checker:
             bad = post["half"] != own
             assert not bad.any(), (f"half{tag}: {int(bad.sum())} elements differ from the "
                                    f"cast of the GPU's own master")
+
+        # each window in pieces of at most PIECE elements (the oracle's update of one piece
+        # does not depend on any other element), on `threads` host threads
+        PIECE = 1 << 23
+        jobs = []
+        for (i, lo, hi, p), post in zip(pre, posts):
+            for a in range(0, hi - lo, PIECE):
+                b = min(hi - lo, a + PIECE)
+                cut = {k: (None if v is None else v[a:b]) for k, v in p.items()}
+                pcut = {k: (None if v is None else v[a:b]) for k, v in post.items()}
+                jobs.append((i, lo + a, lo + b, cut, pcut))
+        if threads <= 1 or len(jobs) == 1:
+            for j in jobs:
+                compare(*j)
+        else:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                for f in [ex.submit(compare, *j) for j in jobs]:
+                    f.result()
         return gst, d

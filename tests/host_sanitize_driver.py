@@ -51,6 +51,15 @@ try:
     Z.neox_zero1_create(Z.neox_zero1_default_config(), segs)   # fails at the first HIP call
 except Z.NeoxError:
     pass
+# gradients aliasing written arrays, and the allocation-free step's validation
+a = TP.flat_segments([64], [True])[0]
+for alias in (Z.neox_segment(a.half, a.half, a.master, a.exp_avg, a.exp_avg_sq, 64, 0, 0, 0),
+              Z.neox_segment(a.master + 4, a.half, a.master, a.exp_avg, a.exp_avg_sq, 64, 0, 0, 0)):
+    try:
+        Z.neox_zero1_plan(Z.neox_zero1_default_config(), [alias])
+        raise SystemExit("plan accepted an aliased gradient")
+    except Z.NeoxError:
+        pass
 L.neox_zero1_step(None, C.c_float(1e-3), None)
 L.neox_zero1_update_path(None)
 L.neox_zero1_timing_begin(None, 10, 0)

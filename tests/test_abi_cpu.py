@@ -123,7 +123,7 @@ def _fake_seg(n=16, base=0x10000, flags=0):
 
 @pytest.mark.parametrize("field,value", [
     ("beta1", 1.0), ("beta1", -0.1), ("beta2", 1.5), ("eps", -1.0), ("eps", float("nan")),
-    ("weight_decay", -0.01), ("clip_norm", float("inf")), ("predivide_factor", 0.0),
+    ("eps", 0.0), ("eps", 1e-50), ("weight_decay", -0.01), ("clip_norm", float("inf")), ("predivide_factor", 0.0),
     ("dp_world_size", 0), ("dtype", 3), ("scaler_mode", 2), ("growth_interval", 0),
     ("init_scale", 0.0), ("init_scale", 1e39), ("growth_factor", 0.5), ("backoff_factor", 0.0),
     ("backoff_factor", 1.5), ("min_scale", 0.0), ("init_step", -1), ("chunk_elems", 100),
@@ -192,7 +192,28 @@ def test_null_handle_calls():
     assert "null" in Z.neox_zero1_last_error().lower()
     assert L.neox_zero1_timing_begin(None, 4, 0) == Z.NEOX_EINVAL
     assert L.neox_zero1_step_local(None, None, None) == Z.NEOX_EINVAL
-    assert L.neox_zero1_step_apply(None, None, C.c_float(1e-3), None) == Z.NEOX_EINVAL
+    assert L.neox_zero1_step_apply(None, None, 1, C.c_float(1e-3), None) == Z.NEOX_EINVAL
     assert L.neox_scaler_set(None, None, None) == Z.NEOX_EINVAL
     assert L.neox_zero1_segment_sumsq(None, None, 0) == Z.NEOX_EINVAL
     assert L.neox_zero1_update_path(None) == Z.NEOX_EINVAL
+
+
+def test_plan_rejects_gradients_aliasing_written_arrays():
+    """A gradient that overlaps a written array (its own half copy, or another segment's
+    master) would be read while other blocks overwrite it: rejected at validation."""
+    a = _fake_seg(16, 0x10000)
+    b = _fake_seg(16, 0x80000)
+    cfg = Z.neox_zero1_default_config()
+    Z.neox_zero1_plan(cfg, [a, b], tables=False)       # disjoint: accepted
+    own_half = Z.neox_segment(a.half, a.half, a.master, a.exp_avg, a.exp_avg_sq, 16, 0, 0, 0)
+    into_master = Z.neox_segment(b.master + 8, b.half, b.master, b.exp_avg, b.exp_avg_sq,
+                                 16, 0, 0, 0)
+    for segs in ([own_half], [a, Z.neox_segment(a.master + 8, b.half, b.master, b.exp_avg,
+                                                b.exp_avg_sq, 16, 0, 0, 0)], [into_master]):
+        with pytest.raises(Z.NeoxError) as e:
+            Z.neox_zero1_plan(cfg, segs, tables=False)
+        assert e.value.code == Z.NEOX_EINVAL and "grad overlaps" in str(e.value)
+    # two segments may read the same gradient (nothing writes it)
+    shared = Z.neox_segment(a.grad, b.half, b.master, b.exp_avg, b.exp_avg_sq, 16, 0, 0, 0)
+    Z.neox_zero1_plan(cfg, [a, shared], tables=False)
+

@@ -39,7 +39,9 @@ def sample_windows(shard, seed, nwin=24, wlen=1 << 15, ends=2048, max_segments=6
     return out
 
 
-def run(w, checked_steps, threads=8, windows_seed=0, **cfg_over):
+def run(w, checked_steps, threads=8, windows_seed=0, full_steps=(), **cfg_over):
+    """Steps w on the GPU and the oracle; on checked_steps the oracle scans the whole
+    gradient and recomputes sampled windows, on full_steps every element."""
     shard = DeviceShard(w)
     shard.init_()
     chk = Checker(shard, **cfg_over)
@@ -48,7 +50,10 @@ def run(w, checked_steps, threads=8, windows_seed=0, **cfg_over):
         for k in range(w.steps):
             shard.grads_(k, chk.scale())
             injected = bool(w.injections.get(k))
-            if k in checked_steps:
+            if k in full_steps:
+                log(f"  {w.name} step {k}: full scan + every element of every segment")
+                chk.step(w.hyper.lr, windows=None, threads=threads, where=f" {w.name} step {k}")
+            elif k in checked_steps:
                 log(f"  {w.name} step {k}: full scan + {len(wins)} windows")
                 chk.step(w.hyper.lr, windows=wins, threads=threads, where=f" {w.name} step {k}")
             else:
@@ -124,10 +129,12 @@ def test_pythia410m_eight_ranks_equal_unsharded():
 
 
 def test_neox20b_shard_100_steps():
-    """215,000,000-param shard, 9 segments, 100 steps, default launch shape."""
+    """215,000,000-param shard, 9 segments, 100 steps, default launch shape: every one of
+    the 215M elements of master, exp_avg, exp_avg_sq and the half copy against the oracle
+    on the first and the last step, sampled windows on steps 1 and 50."""
     w = W.neox20b_shard()
     log("case neox20b shard")
-    chk = run(w, checked_steps={0, 1, 50, 99})
+    chk = run(w, checked_steps={1, 50}, full_steps={0, 99}, threads=16)
     assert chk.ost.step == 100 and chk.ost.skipped_total == 0
 
 

@@ -103,8 +103,8 @@ def test_split_step_with_telemetry_and_sgd(optimizer):
 @pytest.mark.parametrize("D", [4, 8])
 def test_split_step_ranks_match_the_global_oracle(D):
     """D ZeRO-1 ranks of one model on this GPU, one after another: each runs step_local,
-    the D local squared norms are summed in rank order on the host and handed to every
-    rank's step_apply.  Decisions equal the oracle's on the whole model every step,
+    the D local squared norms are gathered in rank order and every rank's step_apply adds
+    them (the same bits on every rank).  Decisions equal the oracle's on the whole model every step,
     clipping is active, an inf in one rank's shard skips every rank, and every rank's
     elements match the oracle's global step."""
     tensors = [(50_000, True), (1_000, False), (120_011, True), (7, False), (30_000, True),
@@ -147,15 +147,17 @@ def test_split_step_ranks_match_the_global_oracle(D):
             pre = [rk["shard"].host_window(i, 0, s["grad"].numel())
                    for rk in ranks for i, s in enumerate(rk["shard"].segs)]
             d = O.decide(ocfg, ost, of, sumsq)
-            # the ranks: local norms, rank-order sum on the host, apply
+            # the ranks: local norms, gathered in rank order (an all-gather's result) into
+            # every rank's copy of the array, then apply (the library adds them)
             for rk in ranks:
                 Z.neox_zero1_step_local(rk["chk"].handle, rk["loc"].data_ptr(), stream)
-            total_sumsq = 0.0
+            gathered = torch.cat([rk["loc"] for rk in ranks])
             for rk in ranks:
-                total_sumsq += float(rk["loc"].item())
-            for rk in ranks:
-                rk["glob"].fill_(total_sumsq)
-                Z.neox_zero1_step_apply(rk["chk"].handle, rk["glob"].data_ptr(), float(lr), stream)
+                rk["glob"] = gathered.clone()
+                Z.neox_zero1_step_apply(rk["chk"].handle, rk["glob"].data_ptr(), float(lr), stream,
+                                        nranks=D)
+            sums = {Z.neox_scaler_state(rk["chk"].handle).last_sumsq for rk in ranks}
+            assert len(sums) == 1, sums                  # the same bits on every rank
             j = 0
             for r, rk in enumerate(ranks):
                 st = Z.neox_scaler_state(rk["chk"].handle)
@@ -405,17 +407,20 @@ def test_timing_events_record_and_change_nothing():
             both(k)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3
-        sums, n = Z.neox_zero1_timing_end(ha)
+        sums, n, per = Z.neox_zero1_timing_end(ha, per_step=3)
         assert n == 3 and all(s > 0.0 for s in sums), (n, sums)
         assert sum(sums) < wall_ms, (sums, wall_ms)
+        # each step spans its three kernels and the gaps between them
+        assert len(per) == 3 and sum(sums) <= sum(per) * 1.0001 and sum(per) < wall_ms, (per, sums)
         assert sums[2] > sums[1]                         # the update outlasts the finalize
         Z.neox_zero1_timing_begin(ha, 5)                 # discarded by the next begin
         both(4)
         Z.neox_zero1_timing_begin(ha, 5, update_only=True)
         for k in range(5, 7):
             both(k)
-        sums, n = Z.neox_zero1_timing_end(ha)
+        sums, n, per = Z.neox_zero1_timing_end(ha, per_step=8)
         assert n == 2 and sums[0] == 0.0 and sums[1] == 0.0 and sums[2] > 0.0, (n, sums)
+        assert len(per) == 2 and abs(sum(per) - sums[2]) <= 1e-6 * sums[2] + 1e-9, (per, sums)
         sa, sb = Z.neox_scaler_state(ha), Z.neox_scaler_state(hb)
         assert sa.step == sb.step == 7 and sa.last_sumsq == sb.last_sumsq
         oa, ob = _outputs(a), _outputs(b)

@@ -206,7 +206,7 @@ def test_parity_after_restored_step_count(t0):
 _DEGENERATE = {
     "zero_grad": {},                                # gradient all zero: norm 0, only decay moves w
     "betas_zero": dict(beta1=0.0, beta2=0.0),       # Adam reduces to g / (|g| + eps)
-    "eps_zero": dict(eps=0.0),
+    "eps_tiny": dict(eps=1e-45),                    # smallest positive FP32 (eps 0 is refused)
     "lr_zero": {},                                  # w and half unchanged, m and v move
     "no_decay": dict(weight_decay=0.0),
 }
@@ -391,11 +391,13 @@ def test_argument_errors_enqueue_nothing():
         d = torch.zeros(2, dtype=torch.float64, device="cuda")
         for lr in (float("nan"), float("inf"), float("-inf")):
             assert L.neox_zero1_step(C.c_void_p(h), C.c_float(lr), C.c_void_p(stream)) == Z.NEOX_EINVAL
-            assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(d.data_ptr()), C.c_float(lr),
+            assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(d.data_ptr()), 1, C.c_float(lr),
                                            C.c_void_p(stream)) == Z.NEOX_EINVAL
         odd = d.data_ptr() + 4
         assert L.neox_zero1_step_local(C.c_void_p(h), C.c_void_p(odd), C.c_void_p(stream)) == Z.NEOX_EINVAL
-        assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(odd), C.c_float(1e-3),
+        assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(odd), 1, C.c_float(1e-3),
+                                       C.c_void_p(stream)) == Z.NEOX_EINVAL
+        assert L.neox_zero1_step_apply(C.c_void_p(h), C.c_void_p(d.data_ptr()), 0, C.c_float(1e-3),
                                        C.c_void_p(stream)) == Z.NEOX_EINVAL
         assert L.neox_zero1_step_local(C.c_void_p(h), None, C.c_void_p(stream)) == Z.NEOX_EINVAL
         out = (C.c_double * 2)()

@@ -139,6 +139,21 @@ def test_beta_zero_is_sign_descent():
         assert ulps32(s["master"], want.astype(np.float32)).max() <= 1
 
 
+def test_eps_zero_is_undefined_at_a_zero_gradient():
+    """With eps = 0 Adam's direction m_hat / sqrt(v_hat) is 0 / 0 wherever the gradient
+    and both moments are zero (a padding element, an unused embedding row), so the
+    master weight becomes NaN: the reason the library requires eps > 0.  Elements with a
+    nonzero gradient stay finite."""
+    cfg = O.Config(eps=0.0, weight_decay=0.0)
+    st = O.Scaler(loss_scale=1.0)
+    s = make_state(4, 11)
+    grad = grads_from([0.0, 1e-3, 0.0, -2e-3])
+    run_step(cfg, st, np.float32(1e-3), grad, s, decay=False)
+    assert st.step == 1 and not st.last_skipped
+    assert np.isnan(s["master"][[0, 2]]).all()
+    assert np.isfinite(s["master"][[1, 3]]).all()
+
+
 def test_decay_only_and_identity():
     """g = 0: moments stay 0 and the update is pure decoupled decay, w*(1-lr*wd);
     a no-decay segment is left bitwise unchanged."""
@@ -530,3 +545,47 @@ def test_sgd_zero_momentum_is_plain_sgd_and_skip_is_untouched():
     for k in s:
         assert np.array_equal(s[k], before[k])
     assert st.last_skipped == 1 and st.step == 3
+
+
+def test_pieces_cover_every_element_once():
+    """The all-core baseline's static partition: contiguous pieces of the concatenation,
+    in order, each element exactly once, piece lengths differing by at most one."""
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        sizes = [int(x) for x in rng.integers(1, 50, int(rng.integers(1, 8)))]
+        parts = int(rng.integers(1, 12))
+        got = O.pieces(sizes, parts)
+        assert len(got) == parts
+        flat = [(k, i) for runs in got for k, lo, hi in runs for i in range(lo, hi)]
+        assert flat == [(k, i) for k, n in enumerate(sizes) for i in range(n)]
+        lens = [sum(hi - lo for _, lo, hi in runs) for runs in got]
+        assert max(lens) - min(lens) <= 1
+
+
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_parallel_step_equals_the_serial_step(threads):
+    """The threaded composition of scan / decide / update over static pieces gives the
+    serial step's arrays bit for bit (clipping inactive, so the norm's summation order
+    only moves its last bits) and its decisions."""
+    sizes, rng = [1000, 3, 20_000, 7, 4096], np.random.default_rng(13)
+
+    def shard():
+        out = []
+        for i, n in enumerate(sizes):
+            s = make_state(n, 20 + i)
+            s["grad"] = grads_from(rng.standard_normal(n) * 1e-4 * 65536)
+            s["decay"] = i % 2 == 0
+            out.append(s)
+        return out
+
+    a = shard()
+    b = [{k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in s.items()} for s in a]
+    sa, sb = O.Scaler(), O.Scaler()
+    for _ in range(3):
+        O.step(O.Config(), sa, np.float32(6e-4), a)
+        O.step_parallel(O.Config(), sb, np.float32(6e-4), b, threads)
+        assert (sa.step, sa.loss_scale, sa.skipped_total) == (sb.step, sb.loss_scale, sb.skipped_total)
+        assert abs(sa.last_sumsq - sb.last_sumsq) <= 1e-12 * sa.last_sumsq and sa.last_coef == 1.0
+        for x, y in zip(a, b):
+            for k in ("half", "master", "m", "v"):
+                assert np.array_equal(x[k], y[k]), k

@@ -28,8 +28,8 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     so = str(tmp_path / "libneox_zero1_san.so")
-    src = [os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
-           for f in ("zero1_kernels.hip", "zero1_api.hip")]
+    sys.path.insert(0, ROOT)
+    from mixed_precision_zero_amd.build import SOURCES as src
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                     "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
