@@ -331,6 +331,29 @@ int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint
                     uint32_t* tile_words, uint64_t word_cap, uint32_t* changes,
                     uint64_t change_cap);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): one whole step -- the same kernels and
+ * launch shapes as neox_zero1_step, so the same bits for the same inputs -- with no
+ * handle and no device allocation.  cfg and segs[nseg] are as for neox_zero1_create
+ * (host memory; segment_norms must be 0).  *state (host) is read for the scaler state
+ * before the step (loss_scale, good_steps, step, skipped_total, consecutive_overflows;
+ * the other fields are ignored) and overwritten with the state after it, as
+ * neox_scaler_state reports it (device_loss_scale = NULL).  The call waits for hip_stream
+ * before it returns.
+ * The library's side of the step (state block, per-block partial sums, work tables) lives
+ * in a fixed device array of NEOX_NOALLOC_SCRATCH_BYTES that each device holds for the
+ * life of the process: about 4.2 bytes per 1,000 elements on a flat partition (up to
+ * ~4e9 elements) and 32 per 1,000 on other layouts (up to ~5e8).  A larger shard is
+ * rejected with NEOX_EINVAL.  Every call on one device uses the same array: calls on one
+ * device from several host threads are serialized by the library; calls from several
+ * processes each have their own array.
+ * Errors: NEOX_EINVAL (as neox_zero1_create, plus null state, bad state values,
+ * non-finite lr, segment_norms, a shard beyond the scratch size), NEOX_ENOMEM (host),
+ * NEOX_EHIP. */
+#define NEOX_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int neox_zero1_step_noalloc(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg,
+                            neox_scaler_state_t* state, float lr, void* hip_stream);
+
 /* Text of the last error raised on the calling thread (never NULL). */
 const char* neox_zero1_last_error(void);
 

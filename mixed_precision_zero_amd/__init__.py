@@ -82,7 +82,8 @@ EXPORTS = ("neox_zero1_default_config", "neox_zero1_partition", "neox_zero1_crea
            "neox_zero1_step_local", "neox_zero1_step_apply", "neox_scaler_set",
            "neox_zero1_segment_sumsq",
            "neox_zero1_timing_begin", "neox_zero1_timing_end", "neox_zero1_update_path",
-           "neox_zero1_plan", "neox_zero1_last_error")
+           "neox_zero1_plan", "neox_zero1_step_noalloc", "neox_zero1_last_error")
+NEOX_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _lib = None
 
@@ -117,6 +118,8 @@ def lib():
         L.neox_zero1_plan.argtypes = [P(neox_zero1_config), P(neox_segment), C.c_uint64,
                                       P(neox_zero1_plan_t), P(neox_chunk_info), C.c_uint64,
                                       P(C.c_uint32), C.c_uint64, P(C.c_uint32), C.c_uint64]
+        L.neox_zero1_step_noalloc.argtypes = [P(neox_zero1_config), P(neox_segment), C.c_uint64,
+                                              P(neox_scaler_state_t), C.c_float, C.c_void_p]
         L.neox_zero1_last_error.argtypes = []
         L.neox_zero1_last_error.restype = C.c_char_p
         for name in EXPORTS:
@@ -246,6 +249,16 @@ def neox_zero1_plan(cfg: neox_zero1_config, segs, tables: bool = True):
     _check(lib().neox_zero1_plan(C.byref(cfg), arr, len(segs), C.byref(plan), chunks,
                                  plan.update_chunks, words, nw, changes, plan.flat_changes))
     return plan, list(chunks[:plan.update_chunks]), list(words[:nw]), list(changes[:plan.flat_changes])
+
+
+def neox_zero1_step_noalloc(cfg: neox_zero1_config, segs, state: neox_scaler_state_t, lr: float,
+                            stream_ptr: int = 0) -> neox_scaler_state_t:
+    """One step with no handle and no device allocation; `state` (the scaler state before
+    the step) is overwritten with the state after it and returned.  Waits for the stream."""
+    arr = (neox_segment * max(1, len(segs)))(*segs)
+    _check(lib().neox_zero1_step_noalloc(C.byref(cfg), arr, len(segs), C.byref(state),
+                                         C.c_float(lr), C.c_void_p(stream_ptr)))
+    return state
 
 
 def neox_zero1_timing_end(h: int, per_step: int = 0):

@@ -5,7 +5,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SO = os.path.join(PKG, "libneox_zero1.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("zero1_kernels.hip", "zero1_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("zero1_kernels.hip", "zero1_api.hip",
+                                                   "zero1_noalloc.hip")]
 PROBE_SO = os.path.join(PKG, "libneox_stream_probe.so")
 PROBE_SOURCES = [os.path.join(PKG, "csrc", "stream_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -60,6 +60,16 @@ for alias in (Z.neox_segment(a.half, a.half, a.master, a.exp_avg, a.exp_avg_sq, 
         raise SystemExit("plan accepted an aliased gradient")
     except Z.NeoxError:
         pass
+st = Z.neox_scaler_state_t()
+st.loss_scale = 65536.0
+for cfg, sg in ((Z.neox_zero1_default_config(chunked_update=1),
+                 [Z.neox_segment(1 << 40, 1 << 41, 1 << 42, (1 << 42) + (1 << 40), 1 << 43,
+                                 600_000_000, 1, 0, 0)]),       # beyond the scratch
+                (Z.neox_zero1_default_config(), segs)):          # fails at the first HIP call
+    try:
+        Z.neox_zero1_step_noalloc(cfg, sg, st, 1e-3)
+    except Z.NeoxError:
+        pass
 L.neox_zero1_step(None, C.c_float(1e-3), None)
 L.neox_zero1_update_path(None)
 L.neox_zero1_timing_begin(None, 10, 0)

@@ -217,3 +217,29 @@ def test_plan_rejects_gradients_aliasing_written_arrays():
     shared = Z.neox_segment(a.grad, b.half, b.master, b.exp_avg, b.exp_avg_sq, 16, 0, 0, 0)
     Z.neox_zero1_plan(cfg, [a, shared], tables=False)
 
+
+def test_noalloc_validates_before_any_device_work():
+    """neox_zero1_step_noalloc refuses bad arguments, and a shard whose work tables do not
+    fit its fixed scratch, before it touches a device (so this runs without a GPU)."""
+    L = Z.lib()
+    cfg = Z.neox_zero1_default_config()
+    st = Z.neox_scaler_state_t()
+    st.loss_scale = 65536.0
+    seg = (Z.neox_segment * 1)(_fake_seg())
+    assert L.neox_zero1_step_noalloc(None, seg, 1, C.byref(st), C.c_float(1e-3), None) == Z.NEOX_EINVAL
+    assert L.neox_zero1_step_noalloc(C.byref(cfg), seg, 1, None, C.c_float(1e-3), None) == Z.NEOX_EINVAL
+    assert L.neox_zero1_step_noalloc(C.byref(cfg), seg, 1, C.byref(st), C.c_float(float("nan")),
+                                     None) == Z.NEOX_EINVAL
+    bad = Z.neox_scaler_state_t()
+    bad.loss_scale = 0.0
+    assert L.neox_zero1_step_noalloc(C.byref(cfg), seg, 1, C.byref(bad), C.c_float(1e-3), None) == Z.NEOX_EINVAL
+    tel = Z.neox_zero1_default_config(segment_norms=1)
+    assert L.neox_zero1_step_noalloc(C.byref(tel), seg, 1, C.byref(st), C.c_float(1e-3), None) == Z.NEOX_EINVAL
+    # 600M elements in separate allocations need ~19 MB of chunk table: beyond 16 MiB
+    n = 600_000_000
+    big = Z.neox_segment(1 << 40, 1 << 41, 1 << 42, (1 << 42) + (1 << 40), 1 << 43, n,
+                         Z.NEOX_SEG_DECAY, 0, 0)
+    with pytest.raises(Z.NeoxError) as e:
+        Z.neox_zero1_step_noalloc(Z.neox_zero1_default_config(chunked_update=1), [big], st, 1e-3)
+    assert e.value.code == Z.NEOX_EINVAL and "scratch" in str(e.value)
+    assert Z.NEOX_NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024
