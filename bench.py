@@ -38,6 +38,34 @@ KERNEL_SRCS = tuple(os.path.join(ROOT, "mixed_precision_zero_amd", "csrc", f)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+PYTHIA_RANKS = {f"pythia410m_dp8_rank{r}": r for r in (0, 1)}
+
+
+def workload_names():
+    import workloads as W
+    return sorted(list(W.BENCH_WORKLOADS) + list(PYTHIA_RANKS))
+
+
+def make_workload(name, partition="library"):
+    """The named workload; a Pythia-410M rank takes its segments from the library's ZeRO-1
+    partition (partition="oracle": the oracle's, for the CPU baseline)."""
+    import workloads as W
+    if name in PYTHIA_RANKS:
+        t = W.pythia410m_tensors()
+        numel, decay = [n for n, _ in t], [d for _, d in t]
+        r = PYTHIA_RANKS[name]
+        if partition == "oracle":
+            from oracle import oracle as O
+            segs, _ = O.partition(numel, decay, 8, r, 64)
+            return W.pythia410m(r, [(g["numel"], g["flags"]) for g in segs])
+        import mixed_precision_zero_amd as Z
+        segs, _ = Z.neox_zero1_partition(numel, decay, 8, r, 64)
+        return W.pythia410m(r, [(g.numel, g.flags) for g in segs])
+    if name not in W.BENCH_WORKLOADS:
+        sys.exit(f"unknown workload {name}; one of {workload_names()}")
+    return W.BENCH_WORKLOADS[name]()
+
+
 def pmc_summary(workload, kernel, optimizer="adamw"):
     """The committed counter summary of one update kernel on one workload."""
     tag = "" if optimizer == "adamw" else f"_{optimizer}"
@@ -102,27 +130,26 @@ def summarize_trace(args):
     import csv
     import glob
 
-    import workloads as W
     files = glob.glob(os.path.join(args.trace, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {args.trace}")
     with open(files[0]) as fh:
         rows = [r for r in csv.DictReader(fh) if "nz1::" in r["Name"]]
-    n = W.BENCH_WORKLOADS[args.workload]().numel
+    n = make_workload(args.workload).numel
     flags = f" {args.bench_flags}" if getattr(args, "bench_flags", "") else ""
     per_param = {"update_kernel": update_bytes(flags_optimizer(args)), "norm_kernel": 2}
     lines = [
         f"# rocprofv3 kernel trace of the ZeRO-1 step on {args.workload} ({n} params), MI355X (gfx950).",
         "# Commands (from the repository root, on an MI355X):",
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 bench.py "
-        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline --skip-steps 0"
-        f"{flags} > <log>",
+        f"--workload {args.workload} --steps {args.trace_steps} --warmup 3 --no-cpu-baseline --skip-steps 0 "
+        f"--no-ceiling --no-extra-workloads{flags} > <log>",
         f"#   python3 bench.py --summarize-trace <dir> --workload {args.workload} "
         f"--trace-steps {args.trace_steps} --bench-log <log>{bench_flags_arg(args)}",
         f"# Calls = 3 warm-up + {args.trace_steps} timed steps (update-kernel events only) + "
-        f"{min(20, args.trace_steps)} steps",
-        "# with events around every kernel; the torch kernels that draw the synthetic inputs and the",
-        "# ceiling probes are left out.  Durations in ns.",
+        f"{args.trace_steps} steps",
+        "# with events around every kernel (a shard whose norm pass has at most 256 blocks has no",
+        "# finalize launch); the torch kernels that draw the synthetic inputs are left out.  Durations in ns.",
         f"kernel_source_sha256: {kernel_sha()}",
         f"{'kernel':44s} {'calls':>6s} {'avg_ns':>10s} {'min_ns':>10s} {'max_ns':>10s}",
     ]
@@ -185,8 +212,7 @@ def summarize_pmc(args):
     cwrite, _ = avg(args.pmc_copy_write, "WRITE_SIZE", "MulFunctor")
     known_kib = args.copy_bytes / 1024.0
     ff, fw = known_kib / cfetch, known_kib / cwrite
-    import workloads as W
-    n = W.BENCH_WORKLOADS[args.workload]().numel
+    n = make_workload(args.workload).numel
     traffic = (fetch * ff + write * fw) * 1024.0
     flags = f" {args.bench_flags}" if getattr(args, "bench_flags", "") else ""
     opt = flags_optimizer(args)
@@ -194,12 +220,12 @@ def summarize_pmc(args):
     lines = [
         f"# HBM traffic of the update on {args.workload} ({n} params), from rocprofv3 PMC.",
         "# Commands (from the repository root, on an MI355X):",
-        f"#   rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> --output-format csv -- python3 bench.py "
-        f"--workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline --no-timing-events --skip-steps 0"
-        f"{flags}",
+        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'nz1::' -d <fetch_dir> --output-format csv "
+        f"-- python3 bench.py --workload {args.workload} --steps 5 --warmup 1 --no-cpu-baseline "
+        f"--no-timing-events --skip-steps 0 --no-ceiling --no-extra-workloads{flags}",
         "#   rocprofv3 --pmc WRITE_SIZE -d <write_dir> ... (same program)",
-        f"#   rocprofv3 --pmc FETCH_SIZE -d <copy_fetch_dir> --output-format csv -- python3 bench.py "
-        f"--copy-probe-only {args.copy_bytes}",
+        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'MulFunctor' -d <copy_fetch_dir> "
+        f"--output-format csv -- python3 bench.py --copy-probe-only {args.copy_bytes}",
         "#   rocprofv3 --pmc WRITE_SIZE -d <copy_write_dir> ... (same program)",
         f"#   python3 bench.py --summarize-pmc --workload {args.workload} --copy-bytes "
         f"{args.copy_bytes} --pmc-fetch <fetch_dir> --pmc-write <write_dir> "
@@ -455,8 +481,6 @@ def cpu_baseline(w, budget_s=10.0):
     """The CPU oracle on this host: the bench workload in full, on all the cores this
     process may use (up to the box's share) and on one thread, plus the two small
     workloads on all cores.  Same seeded inputs as the GPU side (host draws)."""
-    import workloads as W
-
     info = host_info()
     threads = max(1, min(CPU_THREADS_MAX, info["affinity_cpus"]))
     cfg, st, segs, n = _oracle_setup(w)
@@ -465,8 +489,8 @@ def cpu_baseline(w, budget_s=10.0):
     rate_1, steps_1, sec_1 = _time_oracle(cfg, st, segs, n, 1, budget_s, 3)
     del segs
     small = {}
-    for name, mk in (("tiny_1m", W.tiny), ("pythia410m_dp8_rank0", lambda: W.pythia410m(0))):
-        sw = mk()
+    for name in ("tiny_1m", "pythia410m_dp8_rank0"):
+        sw = make_workload(name, partition="oracle")
         c, s2, sg, k = _oracle_setup(sw)
         r, ns, sec = _time_oracle(c, s2, sg, k, threads, 1.0, 20)
         small[name] = {"value": r, "params": k, "steps": ns, "seconds": round(sec, 2),
@@ -612,7 +636,7 @@ def extra_workload(name, dev, steps, warmup):
 
     import mixed_precision_zero_amd as Z
     import workloads as W
-    w = W.BENCH_WORKLOADS[name]()
+    w = make_workload(name)
     n = w.numel
     print(f"[bench] workload {name}: {n} params, {len(w.segments)} segments", file=sys.stderr,
           flush=True)
@@ -636,6 +660,7 @@ def extra_workload(name, dev, steps, warmup):
         gc.collect()
         torch.cuda.empty_cache()
     upd_gbs = UPDATE_BYTES_PER_PARAM * n / (t["update_ms"] * 1e-3) / 1e9
+    upd_name = "flat_update_kernel" if flat_path else "update_kernel"
     return {"params": n, "segments": len(w.segments),
             "layout": "flat shard" if w.flat else "separate allocations",
             "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
@@ -645,9 +670,10 @@ def extra_workload(name, dev, steps, warmup):
             "ms_per_step": t["wall_ms"], "ms_per_step_median": t["step_median_ms"],
             "ms_per_step_min": t["step_min_ms"],
             "step_gbps": STEP_BYTES_PER_PARAM * n / (t["wall_ms"] * 1e-3) / 1e9,
-            "roofline": {"bound": "hbm", "kernel": "flat_update_kernel" if flat_path else "update_kernel",
+            "roofline": {"bound": "hbm", "kernel": upd_name,
                          "achieved": upd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": upd_gbs / HBM_PEAK_GBS, "avg_ms": t["update_ms"],
+                         "traffic": read_traffic(name, n, upd_name),
                          "bytes_per_launch": UPDATE_BYTES_PER_PARAM * n},
             "kernel_avg_ms": {"norm": t["norm_ms"], "finalize": t["finalize_ms"],
                               "update": t["update_ms"]}}
@@ -728,9 +754,7 @@ def main():
     import mixed_precision_zero_amd as Z
     import workloads as W
 
-    if args.workload not in W.BENCH_WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; one of {sorted(W.BENCH_WORKLOADS)}")
-    w = W.BENCH_WORKLOADS[args.workload]()
+    w = make_workload(args.workload)
     sgd = args.optimizer == "sgd"
     w.hyper.optimizer = 1 if sgd else 0
     n = w.numel

@@ -210,7 +210,11 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
  * over every gradient, a one-block finalize (skip decision, clip coefficient, step
  * count, bias corrections, loss-scale update, all on the device), and the fused
  * unscale + clip + AdamW + cast update, which returns before loading its data when the
- * finalize decided to skip.  The gradient must be complete in stream order before this
+ * finalize decided to skip.  When the norm pass has at most 256 blocks (shards up to
+ * ~8M elements; below ~2M its chunks are shortened so that it still spreads over the
+ * chip) there is no separate finalize: every update block sums the partials in the
+ * finalize's order and takes the same decisions itself (same bits), and one of them
+ * writes the state.  The gradient must be complete in stream order before this
  * call.
  * On a skipped step master, exp_avg, exp_avg_sq and half are not written.
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
@@ -274,7 +278,8 @@ int neox_zero1_segment_sumsq(neox_zero1* h, double* out, uint64_t nseg);
  * added to the stream).  The events skip the system-scope fence at completion: they
  * give elapsed times only and order nothing.  neox_zero1_timing_end() waits, writes
  * the summed kernel durations in milliseconds of the norm pass, the finalize and the
- * update to ms_sums[3] (host; the first two are 0 with update_only), the number of
+ * update to ms_sums[3] (host; the first two are 0 with update_only, the finalize's is 0
+ * when the update takes the decisions itself), the number of
  * recorded steps to *steps, and, when step_cap > 0, each of the first step_cap recorded
  * steps' duration to the host array step_ms (from the norm pass's start to the update's
  * end, launch gaps included; the update kernel alone with update_only), then stops

@@ -44,7 +44,7 @@ namespace {
 // Work-unit sizes (elements), measured best on MI355X: the update wants small blocks
 // (2,048 elements: 128 threads x two 16-byte vectors per array) at 2 blocks per CU, the
 // read-only norm pass more bytes per block (32K elements, 8 loads in flight per thread)
-// at 3 blocks per CU.
+// at 4 blocks per CU.
 #ifndef NZ1_UPDATE_CHUNK
 #define NZ1_UPDATE_CHUNK 2048
 #endif
@@ -56,9 +56,10 @@ namespace {
 #ifndef NZ1_UPDATE_BLOCKS_PER_CU
 #define NZ1_UPDATE_BLOCKS_PER_CU 2
 #endif
-// The norm pass: 3 blocks per CU measured 64.7 us on the 215M shard against 66.2 at 4.
+// The norm pass: 4 blocks per CU measured 62.8-63.2 us on the 215M shard against
+// 64.9-65.0 at 3 and 79.5-79.7 at 2 (same process, alternating builds).
 #ifndef NZ1_NORM_BLOCKS_PER_CU
-#define NZ1_NORM_BLOCKS_PER_CU 3
+#define NZ1_NORM_BLOCKS_PER_CU 4
 #endif
 #ifndef NZ1_FLAT_BLOCKS_PER_CU
 #define NZ1_FLAT_BLOCKS_PER_CU 2
@@ -86,26 +87,18 @@ struct TimingSlot {
 struct neox_zero1 {
     neox_zero1_config cfg;
     int device = 0;
-    uint32_t nchunks = 0;          // update work units
-    uint32_t nnorm = 0;            // norm-pass work units
-    uint32_t norm_blocks = 0;
-    uint32_t update_lds = 0;       // LDS reserved per update block (occupancy cap)
-    uint32_t norm_lds = 0;         // LDS reserved per norm block
-    uint32_t flat_lds = 0;         // LDS reserved per flat-update block
-    bool flat = false;             // update runs flat_update_kernel over `span`
-    FlatSpan span{};
+    StepLaunch sl;                 // the step's launches, device addresses resolved
+    // library-owned device memory
     uint32_t* d_tile_word = nullptr;
     uint32_t* d_change = nullptr;
     Chunk* d_chunks = nullptr;
     Chunk* d_norm_chunks = nullptr;
-    uint32_t nseg = 0;
     uint32_t* d_seg_range = nullptr;   // per segment: [first, end) norm chunk (telemetry)
     double* d_seg_sumsq = nullptr;     // per segment squared norm of the last step
     double* d_partial = nullptr;
-    DevState* d_state = nullptr;
+    DevState* d_state = nullptr;       // [0] the state block, [1] the pre-step snapshot
+    uint32_t nseg = 0;
     hipStream_t last_stream = nullptr;
-    FinalizeArgs fin{};
-    UpdateArgs upd_base{};
     // profiling
     std::vector<TimingSlot> timing;
     int64_t timing_used = 0;
@@ -416,12 +409,15 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
     if (cfg->segment_norms && nseg >= (1u << 24))
         return set_error(NEOX_EINVAL, "segment_norms supports fewer than 2^24 segments");
 
-    // update chunks of C elements; norm chunks of the smallest multiple of C that is
-    // at least kNormChunk
+    // update chunks of C elements; norm chunks of the smallest multiple of C that is at
+    // least kNormChunk, or, on a small shard, at least numel / kNormTargetBlocks (so its
+    // norm pass still spreads over the chip)
     p.C = cfg->chunk_elems ? cfg->chunk_elems : kDefaultChunk;
-    const uint64_t C1_64 = p.C >= kNormChunk ? p.C : (uint64_t)(kNormChunk + p.C - 1) / p.C * p.C;
-    p.C1 = C1_64 > (1u << 24) ? p.C : (uint32_t)C1_64;
     for (uint64_t k = 0; k < nseg; ++k) p.numel += segs[k].numel;
+    const uint64_t spread = (p.numel + kNormTargetBlocks - 1) / kNormTargetBlocks;
+    const uint64_t target = spread < kNormChunk ? (spread > p.C ? spread : p.C) : kNormChunk;
+    const uint64_t C1_64 = (target + p.C - 1) / p.C * p.C;
+    p.C1 = C1_64 > (1u << 24) ? p.C : (uint32_t)C1_64;
     try {
         build_chunks(segs, nseg, p.C, p.table);
         build_chunks(segs, nseg, p.C1, p.norm_table);
@@ -430,6 +426,10 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
     }
     // one block per chunk; the grid's x size in work-items is 32-bit
     if (p.table.size() >= (1ull << 24)) return set_error(NEOX_EINVAL, "%zu chunks: raise chunk_elems", p.table.size());
+#if NZ1_SORT_CHUNKS
+    std::stable_sort(p.table.begin(), p.table.end(),
+                     [](const Chunk& a, const Chunk& b) { return (uintptr_t)a.master < (uintptr_t)b.master; });
+#endif
 
     const bool has_v = cfg->optimizer == NEOX_OPT_ADAMW;
     uint64_t flat_n = 0;
@@ -571,23 +571,18 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     neox_zero1* h = new (std::nothrow) neox_zero1();
     if (!h) return set_error(NEOX_ENOMEM, "host allocation of the handle");
     h->cfg = *cfg;
-    h->nchunks = (uint32_t)table.size();
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    StepLaunch& sl = h->sl;
 
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) { free_handle(h); return set_hip_error(e, "hipGetDevice"); }
-    LdsReserve lds;
-    int rc2 = lds_reserve(h->device, cfg->optimizer, &lds);
+    int rc2 = lds_reserve(h->device, cfg->optimizer, &sl.lds);
     if (rc2) { free_handle(h); return rc2; }
-    h->update_lds = lds.update;
-    h->norm_lds = lds.norm;
-    h->flat_lds = lds.flat;
-    h->nnorm = (uint32_t)norm_table.size();
+    const uint32_t nnorm = (uint32_t)norm_table.size();
     // norm pass: one block per norm chunk unless a smaller striding grid is requested
-    uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : h->nnorm;
-    if (nb > h->nnorm) nb = h->nnorm;
+    uint32_t nb = cfg->norm_blocks ? cfg->norm_blocks : nnorm;
+    if (nb > nnorm) nb = nnorm;
     if (nb == 0) nb = 1;
-    h->norm_blocks = nb;
 
     h->nseg = (uint32_t)nseg;
     std::vector<uint32_t> seg_range;
@@ -599,7 +594,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
             free_handle(h);
             return set_error(NEOX_ENOMEM, "host allocation of the segment ranges");
         }
-        for (uint32_t c = 0; c < h->nnorm; ++c) {
+        for (uint32_t c = 0; c < nnorm; ++c) {
             const uint32_t sg = norm_table[c].seg;
             if (c == 0 || norm_table[c - 1].seg != sg) seg_range[2 * sg] = c;
             seg_range[2 * sg + 1] = c + 1;
@@ -612,7 +607,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_range, seg_range.size() * sizeof(uint32_t));
     if (e == hipSuccess && cfg->segment_norms) e = hipMalloc(&h->d_seg_sumsq, nseg * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&h->d_partial, nb * sizeof(double));
-    if (e == hipSuccess) e = hipMalloc(&h->d_state, sizeof(DevState));
+    if (e == hipSuccess) e = hipMalloc(&h->d_state, 2 * sizeof(DevState));
     if (e == hipSuccess && flat) e = hipMalloc(&h->d_tile_word, tile_word.size() * sizeof(uint32_t));
     if (e == hipSuccess && flat) e = hipMalloc(&h->d_change, (change.size() + 1) * sizeof(uint32_t));
     if (e != hipSuccess) {
@@ -621,9 +616,10 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
                                         : set_hip_error(e, "hipMalloc");
     }
 
-    const DevState st = initial_state(*cfg, (float)cfg->init_scale, cfg->init_good_steps,
-                                      cfg->init_step, cfg->init_skipped,
-                                      cfg->init_consecutive_overflows);
+    const DevState st[2] = {initial_state(*cfg, (float)cfg->init_scale, cfg->init_good_steps,
+                                          cfg->init_step, cfg->init_skipped,
+                                          cfg->init_consecutive_overflows),
+                            DevState{}};
 
     if (!flat)
         e = hipMemcpyAsync(h->d_chunks, table.data(), table.size() * sizeof(Chunk), hipMemcpyHostToDevice, stream);
@@ -633,7 +629,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     if (e == hipSuccess && cfg->segment_norms)
         e = hipMemcpyAsync(h->d_seg_range, seg_range.data(), seg_range.size() * sizeof(uint32_t),
                            hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(h->d_state, &st, sizeof st, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->d_state, st, sizeof st, hipMemcpyHostToDevice, stream);
     if (e == hipSuccess && flat)
         e = hipMemcpyAsync(h->d_tile_word, tile_word.data(), tile_word.size() * sizeof(uint32_t),
                            hipMemcpyHostToDevice, stream);
@@ -643,11 +639,20 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) { free_handle(h); return set_hip_error(e, "upload of the chunk table"); }
 
-    h->fin = finalize_args(*cfg);
-
+    sl.dtype = cfg->dtype;
+    sl.optimizer = cfg->optimizer;
+    sl.norm_chunks = h->d_norm_chunks;
+    sl.nnorm = nnorm;
+    sl.norm_blocks = nb;
+    sl.partial = h->d_partial;
+    sl.st = h->d_state;
+    sl.snap = h->d_state + 1;
+    sl.fused = kFuseSmallGrids && nb <= kFuseMaxParts;
+    sl.fin = finalize_args(*cfg);
+    sl.upd = update_args(*cfg);
+    sl.flat = flat;
     if (flat) {
-        h->flat = true;
-        FlatSpan& sp = h->span;
+        FlatSpan& sp = sl.span;
         sp.grad = static_cast<const uint16_t*>(segs[0].grad);
         sp.half = static_cast<uint16_t*>(segs[0].half);
         sp.master = segs[0].master;
@@ -657,34 +662,61 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
         sp.tile_word = h->d_tile_word;
         sp.change = h->d_change;
         sp.ntiles = (uint32_t)(tile_word.size() - 1);
+    } else {
+        sl.chunks = h->d_chunks;
+        sl.nchunks = (uint32_t)table.size();
     }
-
-    h->upd_base = update_args(*cfg);
+    if (cfg->segment_norms) {
+        sl.seg_range = h->d_seg_range;
+        sl.seg_sumsq = h->d_seg_sumsq;
+        sl.nseg = (uint32_t)nseg;
+    }
 
     h->last_stream = stream;
     *out = h;
     return NEOX_OK;
 }
 
-// norm pass (+ per-segment sums when enabled)
-static hipError_t enqueue_norm(neox_zero1* h, hipStream_t stream, const KernelTiming& t = {}) {
-    hipError_t e = launch_norm(h->cfg.dtype, h->d_norm_chunks, h->nnorm, h->norm_blocks,
-                               h->d_state, h->d_partial, h->norm_lds, stream, t);
-    if (e == hipSuccess && h->cfg.segment_norms)
-        e = launch_segment_sumsq(h->d_partial, h->d_seg_range, h->nseg, h->d_seg_sumsq, stream);
+namespace nz1 {
+
+// norm pass (+ per-segment sums when enabled); snapshots the pre-step state for a fused
+// update
+static hipError_t enqueue_norm(const StepLaunch& s, hipStream_t stream, const KernelTiming& t) {
+    hipError_t e = launch_norm(s.dtype, s.norm_chunks, s.nnorm, s.norm_blocks, s.st, s.partial,
+                               s.fused ? s.snap : nullptr, s.lds.norm, stream, t);
+    if (e == hipSuccess && s.seg_sumsq)
+        e = launch_segment_sumsq(s.partial, s.seg_range, s.nseg, s.seg_sumsq, stream);
     return e;
 }
 
-static hipError_t enqueue_update(neox_zero1* h, float lr, hipStream_t stream,
-                                 const KernelTiming& t = {}) {
-    UpdateArgs u = h->upd_base;
+static hipError_t enqueue_update(const StepLaunch& s, float lr, const FuseIn* fuse,
+                                 hipStream_t stream, const KernelTiming& t) {
+    UpdateArgs u = s.upd;
     u.lr = lr;
-    if (h->flat)
-        return launch_flat_update(h->cfg.dtype, h->cfg.optimizer, h->span, h->d_state, u,
-                                  h->flat_lds, stream, t);
-    return launch_update(h->cfg.dtype, h->cfg.optimizer, h->d_chunks, h->nchunks, h->d_state, u,
-                         h->update_lds, stream, t);
+    if (s.flat)
+        return launch_flat_update(s.dtype, s.optimizer, s.span, s.st, u, fuse, s.lds.flat, stream, t);
+    return launch_update(s.dtype, s.optimizer, s.chunks, s.nchunks, s.st, u, fuse, s.lds.update,
+                         stream, t);
 }
+
+hipError_t enqueue_step(const StepLaunch& s, float lr, hipStream_t stream, const KernelTiming* t3) {
+    const KernelTiming none{};
+    hipError_t e = enqueue_norm(s, stream, t3 ? t3[0] : none);
+    if (s.fused) {
+        const FuseIn f{s.partial, s.norm_blocks, s.snap, s.st, s.fin};
+        if (e == hipSuccess) e = enqueue_update(s, lr, &f, stream, t3 ? t3[2] : none);
+    } else {
+        if (e == hipSuccess) e = launch_finalize(s.partial, s.norm_blocks, s.st, s.fin, stream, t3 ? t3[1] : none);
+        if (e == hipSuccess) e = enqueue_update(s, lr, nullptr, stream, t3 ? t3[2] : none);
+    }
+    return e;
+}
+
+hipError_t enqueue_update_only(const StepLaunch& s, float lr, hipStream_t stream) {
+    return enqueue_update(s, lr, nullptr, stream, KernelTiming{});
+}
+
+}  // namespace nz1
 
 extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
     if (!h) return set_error(NEOX_EINVAL, "handle is NULL");
@@ -692,18 +724,13 @@ extern "C" int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream) {
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     TimingSlot* ts = nullptr;
     if (h->timing_used < (int64_t)h->timing.size()) ts = &h->timing[h->timing_used++];
-
-    const bool all = ts && !h->timing_update_only;
-    KernelTiming tn, tf, tu;
-    if (all) {
-        tn = {ts->ev[0], ts->ev[1]};
-        tf = {ts->ev[2], ts->ev[3]};
+    KernelTiming t3[3];
+    if (ts && !h->timing_update_only) {
+        t3[0] = {ts->ev[0], ts->ev[1]};
+        t3[1] = {ts->ev[2], ts->ev[3]};
     }
-    if (ts) tu = {ts->ev[4], ts->ev[5]};
-    hipError_t e = enqueue_norm(h, stream, tn);
-    if (e == hipSuccess)
-        e = launch_finalize(h->d_partial, h->norm_blocks, h->d_state, h->fin, stream, tf);
-    if (e == hipSuccess) e = enqueue_update(h, lr, stream, tu);
+    if (ts) t3[2] = {ts->ev[4], ts->ev[5]};
+    const hipError_t e = enqueue_step(h->sl, lr, stream, ts ? t3 : nullptr);
     h->last_stream = stream;
     if (e != hipSuccess) return set_hip_error(e, "step launch");
     return NEOX_OK;
@@ -713,8 +740,8 @@ extern "C" int neox_zero1_step_local(neox_zero1* h, double* local_sumsq, void* h
     if (!h || !local_sumsq) return set_error(NEOX_EINVAL, "null argument");
     if ((uintptr_t)local_sumsq & 7u) return set_error(NEOX_EINVAL, "local_sumsq not 8-byte aligned");
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = enqueue_norm(h, stream);
-    if (e == hipSuccess) e = launch_reduce(h->d_partial, h->norm_blocks, local_sumsq, stream);
+    hipError_t e = enqueue_norm(h->sl, stream, KernelTiming{});
+    if (e == hipSuccess) e = launch_reduce(h->sl.partial, h->sl.norm_blocks, local_sumsq, stream);
     h->last_stream = stream;
     if (e != hipSuccess) return set_hip_error(e, "step_local launch");
     return NEOX_OK;
@@ -727,8 +754,8 @@ extern "C" int neox_zero1_step_apply(neox_zero1* h, const double* rank_sumsq, ui
     if ((uintptr_t)rank_sumsq & 7u) return set_error(NEOX_EINVAL, "rank_sumsq not 8-byte aligned");
     if (!std::isfinite(lr)) return set_error(NEOX_EINVAL, "lr %g is not finite", (double)lr);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = launch_finalize(rank_sumsq, nranks, h->d_state, h->fin, stream);
-    if (e == hipSuccess) e = enqueue_update(h, lr, stream);
+    hipError_t e = launch_finalize(rank_sumsq, nranks, h->sl.st, h->sl.fin, stream);
+    if (e == hipSuccess) e = enqueue_update_only(h->sl, lr, stream);
     h->last_stream = stream;
     if (e != hipSuccess) return set_hip_error(e, "step_apply launch");
     return NEOX_OK;
@@ -743,7 +770,7 @@ extern "C" int neox_scaler_set(neox_zero1* h, const neox_scaler_state_t* st, voi
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipError_t e = launch_set_state(h->d_state, st->loss_scale, st->good_steps, st->step,
                                     st->skipped_total, st->consecutive_overflows,
-                                    h->fin.predivide_factor, h->fin.dp_world_size, stream);
+                                    h->sl.fin.predivide_factor, h->sl.fin.dp_world_size, stream);
     h->last_stream = stream;
     if (e != hipSuccess) return set_hip_error(e, "scaler_set launch");
     return NEOX_OK;
@@ -829,6 +856,7 @@ extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* st
         hipError_t r = hipEventSynchronize(s.ev[5]);
         if (r != hipSuccess) return set_hip_error(r, "hipEventSynchronize");
         for (int k = first; k < 3; ++k) {
+            if (k == 1 && h->sl.fused) continue;     // no finalize launch: its time is 0
             float ms = 0.0f;
             r = hipEventElapsedTime(&ms, s.ev[2 * k], s.ev[2 * k + 1]);
             if (r != hipSuccess) return set_hip_error(r, "hipEventElapsedTime");
@@ -849,7 +877,7 @@ extern "C" int neox_zero1_timing_end(neox_zero1* h, double* ms_sums, int64_t* st
 
 extern "C" int neox_zero1_update_path(const neox_zero1* h) {
     if (!h) return set_error(NEOX_EINVAL, "handle is NULL");
-    return h->flat ? NEOX_PATH_FLAT : NEOX_PATH_CHUNKED;
+    return h->sl.flat ? NEOX_PATH_FLAT : NEOX_PATH_CHUNKED;
 }
 
 extern "C" const char* neox_zero1_last_error(void) { return g_last_error.c_str(); }

@@ -99,6 +99,22 @@ struct UpdateArgs {
     float b1, omb1, b2, omb2, eps, wd, lr;
 };
 
+// A norm pass of at most this many blocks hands its partials straight to the update,
+// which then takes the step's decisions itself (no finalize launch).
+constexpr uint32_t kFuseMaxParts = 256;
+#ifndef NZ1_FUSE_SMALL_GRIDS
+#define NZ1_FUSE_SMALL_GRIDS 1
+#endif
+constexpr bool kFuseSmallGrids = NZ1_FUSE_SMALL_GRIDS;
+// Small shards split the norm pass into at least about this many blocks (shorter norm
+// chunks, down to the update chunk length).  On the 1M-element shard: 11.4-11.5 us per
+// step at 64, 11.9-12.1 at 16, 12.7-12.8 at 256 (whose fused update sums four waves of
+// partials), 12.5-13.5 with a separate finalize (same process, alternating builds).
+#ifndef NZ1_NORM_TARGET_BLOCKS
+#define NZ1_NORM_TARGET_BLOCKS 64
+#endif
+constexpr uint32_t kNormTargetBlocks = NZ1_NORM_TARGET_BLOCKS;
+
 // Optional timing of one launch: both null, or two events that receive the kernel's own
 // start and stop time from its dispatch (no marker packets between kernels).
 struct KernelTiming {
@@ -106,9 +122,21 @@ struct KernelTiming {
     hipEvent_t stop = nullptr;
 };
 
+// What an update needs to take the step's decisions itself (small norm grids): the norm
+// pass's nparts <= kFuseMaxParts partials, its snapshot of the pre-step state, and the
+// state block that block 0 writes.
+struct FuseIn {
+    const double* partial;
+    uint32_t nparts;
+    const DevState* snap;
+    DevState* st;
+    FinalizeArgs fin;
+};
+
 // Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
+// snap (optional): the norm pass copies the pre-step state there for a fused update.
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
-                       const DevState* st, double* partial, uint32_t lds_reserve,
+                       const DevState* st, double* partial, DevState* snap, uint32_t lds_reserve,
                        hipStream_t stream, const KernelTiming& t = {});
 // The finalize sums partial[0, nparts) in a fixed order (the norm pass's partials, or the
 // ranks' squared norms of a split step), then takes the step's decisions.
@@ -120,12 +148,14 @@ hipError_t launch_segment_sumsq(const double* partial, const uint32_t* range, ui
 hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64_t step,
                             int64_t skipped, int32_t consecutive, double predivide, double dp,
                             hipStream_t stream);
+// fuse: null (the finalize ran; the update reads its decision from st) or the inputs of
+// the update's own decision.
 hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
-                         const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
-                         hipStream_t stream, const KernelTiming& t = {});
+                         const DevState* st, const UpdateArgs& a, const FuseIn* fuse,
+                         uint32_t lds_reserve, hipStream_t stream, const KernelTiming& t = {});
 hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const DevState* st,
-                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream,
-                              const KernelTiming& t = {});
+                              const UpdateArgs& a, const FuseIn* fuse, uint32_t lds_reserve,
+                              hipStream_t stream, const KernelTiming& t = {});
 
 // Static LDS (bytes) of the norm kernel: launch reservations subtract it so that the
 // requested number of blocks per CU really fits.
@@ -179,5 +209,33 @@ struct LdsReserve {
     uint32_t norm = 0, update = 0, flat = 0;
 };
 int lds_reserve(int device, int optimizer, LdsReserve* out);
+
+// Everything one step launches, with device addresses resolved: what a handle keeps and
+// what the allocation-free entry point assembles in its scratch.
+struct StepLaunch {
+    int dtype = 0, optimizer = 0;
+    const Chunk* norm_chunks = nullptr;
+    uint32_t nnorm = 0, norm_blocks = 0;
+    double* partial = nullptr;            // norm_blocks doubles
+    DevState* st = nullptr;
+    DevState* snap = nullptr;             // pre-step state copy (fused steps)
+    bool fused = false;                   // norm_blocks <= kFuseMaxParts: no finalize launch
+    FinalizeArgs fin{};
+    UpdateArgs upd{};
+    bool flat = false;
+    FlatSpan span{};                      // flat update
+    const Chunk* chunks = nullptr;        // chunked update
+    uint32_t nchunks = 0;
+    LdsReserve lds{};
+    // per-segment telemetry after the norm pass (all null / 0 when off)
+    const uint32_t* seg_range = nullptr;
+    double* seg_sumsq = nullptr;
+    uint32_t nseg = 0;
+};
+// norm -> finalize (unless fused) -> update on stream; t3: null, or timings of the three
+// kernels (the finalize's is not used when fused).
+hipError_t enqueue_step(const StepLaunch& s, float lr, hipStream_t stream, const KernelTiming* t3);
+// the update alone after a finalize has taken the decision (split step)
+hipError_t enqueue_update_only(const StepLaunch& s, float lr, hipStream_t stream);
 
 }  // namespace nz1

@@ -232,11 +232,22 @@ __device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, u
     return block_sum<kBlock>(a0 + a1);
 }
 
+// snap (optional): block 0 copies the scaler state the step starts from, for an update
+// that takes the step's decisions itself (see fused_decide).
 template <int DT>
 __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ chunks,
                                                       uint32_t nchunks,
                                                       const DevState* __restrict__ st,
-                                                      double* __restrict__ partial) {
+                                                      double* __restrict__ partial,
+                                                      DevState* __restrict__ snap) {
+    if (snap && blockIdx.x == 0 && threadIdx.x == 0) {
+        snap->loss_scale = st->loss_scale;
+        snap->inv = st->inv;
+        snap->good_steps = st->good_steps;
+        snap->consecutive_overflows = st->consecutive_overflows;
+        snap->step = st->step;
+        snap->skipped_total = st->skipped_total;
+    }
     const double s = norm_block<DT>(chunks, nchunks, st->inv);
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
@@ -318,59 +329,95 @@ __device__ __forceinline__ double ipow(double b, int64_t t) {
     return r;
 }
 
-// The step's decisions from its squared norm (one thread): skip, clip coefficient, step
-// count, bias corrections and the loss-scale state machine, written to the state block.
-// Each state field is read once, before the decision, and written at the end.
-__device__ __forceinline__ void finalize_state(double sumsq, DevState* __restrict__ st,
-                                               const FinalizeArgs& a) {
-    const float scale0 = st->loss_scale;
-    const float inv_used = st->inv;
-    const int32_t good0 = st->good_steps;
-    const int64_t step0 = st->step;
-    const int64_t skipped0 = st->skipped_total;
-    const int32_t consecutive0 = st->consecutive_overflows;
-    float scale = scale0;
+// The scaler state a step starts from.
+struct PreState {
+    float scale;
+    float inv;                   // unscale factor the norm pass used
+    int32_t good;
+    int32_t consecutive;
+    int64_t step;
+    int64_t skipped;
+};
+__device__ __forceinline__ PreState read_pre(const DevState* __restrict__ st) {
+    return PreState{st->loss_scale, st->inv, st->good_steps, st->consecutive_overflows,
+                    st->step, st->skipped_total};
+}
+
+// The step's decisions from its squared norm: skip, clip coefficient, step count, bias
+// corrections and the loss-scale state machine.  A pure function of its inputs, so every
+// thread that evaluates it gets the same bits.
+struct Decision {
+    DevState next;               // the state block after the step
+};
+__device__ __forceinline__ Decision decide(double sumsq, const PreState& p, const FinalizeArgs& a) {
+    Decision d;
+    DevState& n = d.next;
+    float scale = p.scale;
     if (!f64_finite(sumsq)) {
         // overflow: skip, back off (not below the floor), restart the clean count
-        st->skip = 1;
+        n.skip = 1;
+        n.gscale = 0.0f;
+        n.rbc1 = 0.0f;
+        n.rsbc2 = 0.0f;
         if (a.dynamic) {
             float s = (float)((double)scale * a.backoff_factor);
             scale = s < a.min_scale ? a.min_scale : s;
         }
-        st->good_steps = 0;
-        st->consecutive_overflows = consecutive0 + 1;
-        st->skipped_total = skipped0 + 1;
-        st->last_skipped = 1;
-        st->last_sumsq = 0.0;
-        st->last_grad_norm = __builtin_inff();
-        st->last_clip_coef = 1.0f;
+        n.good_steps = 0;
+        n.consecutive_overflows = p.consecutive + 1;
+        n.skipped_total = p.skipped + 1;
+        n.step = p.step;
+        n.last_skipped = 1;
+        n.last_sumsq = 0.0;
+        n.last_grad_norm = __builtin_inff();
+        n.last_clip_coef = 1.0f;
     } else {
         const double norm = __builtin_sqrt(sumsq);
         double coef = 1.0;
         if (a.clip_norm > 0.0 && norm > a.clip_norm) coef = a.clip_norm / norm;
-        const int64_t t = step0 + 1;
+        const int64_t t = p.step + 1;
         const double bc1 = 1.0 - ipow(a.beta1, t);
         const double bc2 = 1.0 - ipow(a.beta2, t);
-        st->skip = 0;
-        st->gscale = (float)((double)inv_used * coef);
-        st->rbc1 = (float)(1.0 / bc1);
-        st->rsbc2 = (float)(1.0 / __builtin_sqrt(bc2));
-        st->step = t;
-        int32_t good = good0 + 1;
+        n.skip = 0;
+        n.gscale = (float)((double)p.inv * coef);
+        n.rbc1 = (float)(1.0 / bc1);
+        n.rsbc2 = (float)(1.0 / __builtin_sqrt(bc2));
+        n.step = t;
+        int32_t good = p.good + 1;
         if (a.dynamic && good >= a.growth_interval) {
             const float s = (float)((double)scale * a.growth_factor);
             if (f32_finite(s)) scale = s;
             good = 0;
         }
-        st->good_steps = good;
-        st->consecutive_overflows = 0;
-        st->last_skipped = 0;
-        st->last_sumsq = sumsq;
-        st->last_grad_norm = (float)norm;
-        st->last_clip_coef = (float)coef;
+        n.good_steps = good;
+        n.consecutive_overflows = 0;
+        n.skipped_total = p.skipped;
+        n.last_skipped = 0;
+        n.last_sumsq = sumsq;
+        n.last_grad_norm = (float)norm;
+        n.last_clip_coef = (float)coef;
     }
-    st->loss_scale = scale;
-    st->inv = unscale_factor(a.predivide_factor, a.dp_world_size, scale);
+    n.loss_scale = scale;
+    n.inv = unscale_factor(a.predivide_factor, a.dp_world_size, scale);
+    n.pad_[0] = n.pad_[1] = n.pad_[2] = 0;
+    return d;
+}
+
+__device__ __forceinline__ void write_state(DevState* __restrict__ st, const DevState& n) {
+    st->loss_scale = n.loss_scale;
+    st->good_steps = n.good_steps;
+    st->step = n.step;
+    st->skipped_total = n.skipped_total;
+    st->consecutive_overflows = n.consecutive_overflows;
+    st->last_skipped = n.last_skipped;
+    st->last_sumsq = n.last_sumsq;
+    st->last_grad_norm = n.last_grad_norm;
+    st->last_clip_coef = n.last_clip_coef;
+    st->inv = n.inv;
+    st->skip = n.skip;
+    st->gscale = n.gscale;
+    st->rbc1 = n.rbc1;
+    st->rsbc2 = n.rsbc2;
 }
 
 // The squared norm is the fixed-order sum of nparts values: this handle's per-block
@@ -380,7 +427,42 @@ __global__ __launch_bounds__(kFinalizeBlock) void finalize_kernel(const double* 
                                                                   DevState* __restrict__ st,
                                                                   FinalizeArgs a) {
     const double sumsq = sum_partials(partial, nparts);
-    if (threadIdx.x == 0) finalize_state(sumsq, st, a);
+    if (threadIdx.x == 0) write_state(st, decide(sumsq, read_pre(st), a).next);
+}
+
+// For a norm pass of at most kFuseMaxParts blocks the update takes the step's decisions
+// itself and the finalize launch is not made.  Every wave of every update block sums the
+// partials exactly as sum_partials does with kFinalizeBlock threads: thread t < nparts
+// holds 0 + partial[t], the others 0; each wave of the finalize adds its 64 values by the
+// xor-butterfly, and the wave sums are added in wave order.  One wave here walks the
+// finalize's waves in turn with the same butterfly, so the squared norm and every
+// decision have the bits the finalize kernel would give.  The pre-step state comes from
+// the norm pass's snapshot, and block 0 writes the state block.
+static_assert(kFuseMaxParts == kFinalizeBlock && kFinalizeBlock % 64 == 0,
+              "a fused update covers the finalize's whole first pass");
+struct Fuse {
+    const double* partial;       // null: the finalize kernel ran, read the state block
+    uint32_t nparts;
+    const DevState* snap;
+    DevState* st;                // written by block 0
+    FinalizeArgs fin;
+};
+__device__ __forceinline__ Decision fused_decide(const Fuse& f) {
+    const uint32_t lane = threadIdx.x & 63;
+    // finalize waves holding partials; the others sum to +0, which is added as such
+    const uint32_t waves = (f.nparts + 63) / 64;
+    double r = 0.0;
+    for (uint32_t w = 0; w < kFinalizeBlock / 64; ++w) {
+        double v = 0.0;
+        if (w < waves) {
+            const uint32_t i = w * 64 + lane;
+            if (i < f.nparts) v = 0.0 + f.partial[i];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        }
+        r = w == 0 ? v : r + v;
+    }
+    return decide(r, read_pre(f.snap), f.fin);
 }
 
 // ------------------------------------------------------------------------------------
@@ -560,12 +642,13 @@ __device__ __forceinline__ const Chunk* chunk_at(const Chunk* chunks, uint32_t n
     return chunks + (NZ1_UPDATE_REVERSE ? nchunks - 1 - k : k);
 }
 
-// Generic layout: one block per entry of the chunk table.
-template <int DT, int U, int OPT>
+// Generic layout: one block per entry of the chunk table.  FUSE: the block takes the
+// step's decisions from the norm pass's partials itself (small norm grids, no finalize).
+template <int DT, int U, int OPT, bool FUSE>
 __global__ __launch_bounds__(kUpdateBlock) void update_kernel(const Chunk* __restrict__ chunks,
                                                               uint32_t nchunks,
                                                               const DevState* __restrict__ st,
-                                                              UpdateArgs a) {
+                                                              UpdateArgs a, Fuse f) {
     const Chunk* ch = chunk_at(chunks, nchunks, blockIdx.x);
     // The descriptor and the finalize's decision are fetched together: the early exit
     // below tests both, so neither load waits for the other.
@@ -576,8 +659,17 @@ __global__ __launch_bounds__(kUpdateBlock) void update_kernel(const Chunk* __res
     float* __restrict__ wp = ch->master;
     float* __restrict__ mp = ch->m;
     float* __restrict__ vp = ch->v;
-    const int32_t skip = st->skip;
-    const Coefs c{st->gscale, st->rbc1, st->rsbc2};
+    int32_t skip;
+    Coefs c;
+    if constexpr (FUSE) {
+        const Decision d = fused_decide(f);
+        if (blockIdx.x == 0 && threadIdx.x == 0) write_state(f.st, d.next);
+        skip = d.next.skip;
+        c = Coefs{d.next.gscale, d.next.rbc1, d.next.rsbc2};
+    } else {
+        skip = st->skip;
+        c = Coefs{st->gscale, st->rbc1, st->rsbc2};
+    }
     // Chunks are never empty, their pointers are at least 2-byte aligned and flags use
     // the low bits only, so the last two terms never fire; they make the branch wait for
     // the whole descriptor at once.
@@ -645,17 +737,38 @@ __device__ __forceinline__ StepWords ld_after(const DevState* st, const uint32_t
     return r;
 }
 
+// The decision, coefficients and tile words of a flat-update block: from the state block
+// behind the data (ld_after), or, with FUSE, taken by the block itself (block 0 also
+// writes the state block).
+template <bool FUSE>
+__device__ __forceinline__ StepWords step_words(const DevState* st, const uint32_t* word, const Fuse& f) {
+    if constexpr (FUSE) {
+        const Decision d = fused_decide(f);
+        if (blockIdx.x == 0 && threadIdx.x == 0) write_state(f.st, d.next);
+        StepWords r;
+        r.skip = d.next.skip;
+        r.gscale = d.next.gscale;
+        r.rbc1 = d.next.rbc1;
+        r.rsbc2 = d.next.rsbc2;
+        r.w0 = word[0];
+        r.w1 = word[1];
+        return r;
+    } else {
+        return ld_after(st, word);
+    }
+}
+
 // Flat layout: the segments tile five contiguous 16-byte-aligned arrays (a flat
 // partition), so tile T's addresses follow from T alone: a block needs no work
 // descriptor (a per-block load that streaming has evicted to HBM) before its first data
 // load, only the finalize's decision, which every block reads and the L2 keeps.  The
 // tile's decay words and the coefficients are fetched behind the data.
-template <int DT, int OPT>
+template <int DT, int OPT, bool FUSE>
 __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
                                                              const uint32_t* __restrict__ tile_word,
                                                              const uint32_t* __restrict__ change,
                                                              const DevState* __restrict__ st,
-                                                             UpdateArgs a) {
+                                                             UpdateArgs a, Fuse f) {
     constexpr int U = kFlatUnroll;
     const uint32_t T = s.ntiles - 1 - blockIdx.x;     // last tile first, as above
     const uint64_t nvec = s.n / kVec;
@@ -670,9 +783,12 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
     // Wait for the decision before loading: a skipped step then reads nothing here.  The
     // base pointers are 16-byte aligned, so their low-bit term never fires; it makes the
     // branch wait for them too, so they are fetched with the state pointer, not after.
-    const uintptr_t low = ((uintptr_t)s.grad | (uintptr_t)s.half | (uintptr_t)s.master |
-                           (uintptr_t)s.m | (uintptr_t)s.v) & 1u;
-    if (st->skip | (int32_t)low) return;
+    // (With FUSE the decision is not made yet: small shards load speculatively.)
+    if constexpr (!FUSE) {
+        const uintptr_t low = ((uintptr_t)s.grad | (uintptr_t)s.half | (uintptr_t)s.master |
+                               (uintptr_t)s.m | (uintptr_t)s.v) & 1u;
+        if (st->skip | (int32_t)low) return;
+    }
 #endif
     if (T + 1 < s.ntiles || s.n % kFlatTile == 0) {
         // a full tile: every thread owns U whole vectors
@@ -683,7 +799,7 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
             load8<OPT>(g4, w4, m4, v4, v0 + u * kFlatBlock + threadIdx.x, G[u], W[u], M[u], V[u]);
         // Then the decision, the coefficients and the tile words, as vector loads issued
         // behind the data (see ld_after).
-        const StepWords sw = ld_after(st, tile_word + T);
+        const StepWords sw = step_words<FUSE>(st, tile_word + T, f);
         const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
         const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
         const uint32_t start_mask = (sw.w0 & 1u) ? 0xFFu : 0u;
@@ -714,7 +830,7 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
 
     // the last tile, shorter than kFlatTile: guarded vectors, then the last n % 8
     // elements on the scalar path
-    const StepWords sw = ld_after(st, tile_word + T);
+    const StepWords sw = step_words<FUSE>(st, tile_word + T, f);
     if (sw.skip) return;
     const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
     const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
@@ -755,10 +871,10 @@ static void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t ld
 }
 
 hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
-                       const DevState* st, double* partial, uint32_t lds_reserve,
+                       const DevState* st, double* partial, DevState* snap, uint32_t lds_reserve,
                        hipStream_t stream, const KernelTiming& t) {
     launch(dtype == 1 ? norm_kernel<1> : norm_kernel<2>, dim3(blocks), dim3(kBlock), lds_reserve,
-           stream, t, chunks, nchunks, st, partial);
+           stream, t, chunks, nchunks, st, partial, snap);
     return hipGetLastError();
 }
 
@@ -787,28 +903,58 @@ hipError_t launch_set_state(DevState* st, float scale, int32_t good_steps, int64
     return hipGetLastError();
 }
 
-template <int OPT>
+template <int OPT, bool FUSE>
 static void launch_update_opt(int dtype, const Chunk* chunks, uint32_t nchunks, const DevState* st,
-                              const UpdateArgs& a, uint32_t lds, hipStream_t stream,
+                              const UpdateArgs& a, const Fuse& f, uint32_t lds, hipStream_t stream,
                               const KernelTiming& t) {
-    launch(dtype == 1 ? update_kernel<1, kUpdateUnroll, OPT> : update_kernel<2, kUpdateUnroll, OPT>,
-           dim3(nchunks), dim3(kUpdateBlock), lds, stream, t, chunks, nchunks, st, a);
+    launch(dtype == 1 ? update_kernel<1, kUpdateUnroll, OPT, FUSE> : update_kernel<2, kUpdateUnroll, OPT, FUSE>,
+           dim3(nchunks), dim3(kUpdateBlock), lds, stream, t, chunks, nchunks, st, a, f);
 }
 
-template <int OPT>
-static void launch_flat_opt(int dtype, const FlatSpan& f, const DevState* st, const UpdateArgs& a,
-                            uint32_t lds, hipStream_t stream, const KernelTiming& t) {
-    launch(dtype == 1 ? flat_update_kernel<1, OPT> : flat_update_kernel<2, OPT>, dim3(f.ntiles),
-           dim3(kFlatBlock), lds, stream, t, f, f.tile_word, f.change, st, a);
+template <int OPT, bool FUSE>
+static void launch_flat_opt(int dtype, const FlatSpan& sp, const DevState* st, const UpdateArgs& a,
+                            const Fuse& f, uint32_t lds, hipStream_t stream, const KernelTiming& t) {
+    launch(dtype == 1 ? flat_update_kernel<1, OPT, FUSE> : flat_update_kernel<2, OPT, FUSE>,
+           dim3(sp.ntiles), dim3(kFlatBlock), lds, stream, t, sp, sp.tile_word, sp.change, st, a, f);
 }
 
-hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const DevState* st,
-                              const UpdateArgs& a, uint32_t lds_reserve, hipStream_t stream,
-                              const KernelTiming& t) {
+static Fuse fuse_args(const FuseIn* in) {
+    Fuse f{};
+    if (in) {
+        f.partial = in->partial;
+        f.nparts = in->nparts;
+        f.snap = in->snap;
+        f.st = in->st;
+        f.fin = in->fin;
+    }
+    return f;
+}
+
+hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& sp, const DevState* st,
+                              const UpdateArgs& a, const FuseIn* fuse, uint32_t lds_reserve,
+                              hipStream_t stream, const KernelTiming& t) {
+    const Fuse f = fuse_args(fuse);
     if (optimizer == 1)
-        launch_flat_opt<1>(dtype, f, st, a, lds_reserve, stream, t);
+        fuse ? launch_flat_opt<1, true>(dtype, sp, st, a, f, lds_reserve, stream, t)
+             : launch_flat_opt<1, false>(dtype, sp, st, a, f, lds_reserve, stream, t);
     else
-        launch_flat_opt<0>(dtype, f, st, a, lds_reserve, stream, t);
+        fuse ? launch_flat_opt<0, true>(dtype, sp, st, a, f, lds_reserve, stream, t)
+             : launch_flat_opt<0, false>(dtype, sp, st, a, f, lds_reserve, stream, t);
+    return hipGetLastError();
+}
+
+// lds_reserve: dynamic LDS the kernel never touches, requested only to cap how many
+// blocks share a CU (fewer tiles in flight keep the chip's open DRAM rows few).
+hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
+                         const DevState* st, const UpdateArgs& a, const FuseIn* fuse,
+                         uint32_t lds_reserve, hipStream_t stream, const KernelTiming& t) {
+    const Fuse f = fuse_args(fuse);
+    if (optimizer == 1)
+        fuse ? launch_update_opt<1, true>(dtype, chunks, nchunks, st, a, f, lds_reserve, stream, t)
+             : launch_update_opt<1, false>(dtype, chunks, nchunks, st, a, f, lds_reserve, stream, t);
+    else
+        fuse ? launch_update_opt<0, true>(dtype, chunks, nchunks, st, a, f, lds_reserve, stream, t)
+             : launch_update_opt<0, false>(dtype, chunks, nchunks, st, a, f, lds_reserve, stream, t);
     return hipGetLastError();
 }
 
@@ -817,18 +963,6 @@ hipError_t norm_static_lds(uint32_t* bytes) {
     const hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&norm_kernel<1>));
     *bytes = e == hipSuccess ? (uint32_t)a.sharedSizeBytes : 0u;
     return e;
-}
-
-// lds_reserve: dynamic LDS the kernel never touches, requested only to cap how many
-// blocks share a CU (fewer tiles in flight keep the chip's open DRAM rows few).
-hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t nchunks,
-                         const DevState* st, const UpdateArgs& a, uint32_t lds_reserve,
-                         hipStream_t stream, const KernelTiming& t) {
-    if (optimizer == 1)
-        launch_update_opt<1>(dtype, chunks, nchunks, st, a, lds_reserve, stream, t);
-    else
-        launch_update_opt<0>(dtype, chunks, nchunks, st, a, lds_reserve, stream, t);
-    return hipGetLastError();
 }
 
 }  // namespace nz1

@@ -83,7 +83,7 @@ extern "C" int neox_zero1_step_noalloc(const neox_zero1_config* cfg, const neox_
 
     Layout L;
     L.state = 0;
-    L.partial = round256(sizeof(DevState));
+    L.partial = round256(2 * sizeof(DevState));   // the state block and its snapshot
     L.norm_table = round256(L.partial + (size_t)nb * sizeof(double));
     L.table = round256(L.norm_table + plan.norm_table.size() * sizeof(Chunk));
     size_t end = L.table;
@@ -134,40 +134,44 @@ extern "C" int neox_zero1_step_noalloc(const neox_zero1_config* cfg, const neox_
     }
 
     DevState* d_state = reinterpret_cast<DevState*>(base + L.state);
-    double* d_partial = reinterpret_cast<double*>(base + L.partial);
-    const Chunk* d_norm = reinterpret_cast<const Chunk*>(base + L.norm_table);
-    UpdateArgs ua = update_args(*cfg);
-    ua.lr = lr;
-    const FinalizeArgs fa = finalize_args(*cfg);
+    StepLaunch sl;
+    sl.dtype = cfg->dtype;
+    sl.optimizer = cfg->optimizer;
+    sl.norm_chunks = reinterpret_cast<const Chunk*>(base + L.norm_table);
+    sl.nnorm = nnorm;
+    sl.norm_blocks = nb;
+    sl.partial = reinterpret_cast<double*>(base + L.partial);
+    sl.st = d_state;
+    sl.snap = d_state + 1;
+    sl.fused = kFuseSmallGrids && nb <= kFuseMaxParts;
+    sl.fin = finalize_args(*cfg);
+    sl.upd = update_args(*cfg);
+    sl.lds = lds;
+    sl.flat = plan.flat;
+    if (plan.flat) {
+        FlatSpan& sp = sl.span;
+        sp.grad = static_cast<const uint16_t*>(segs[0].grad);
+        sp.half = static_cast<uint16_t*>(segs[0].half);
+        sp.master = segs[0].master;
+        sp.m = segs[0].exp_avg;
+        sp.v = cfg->optimizer == NEOX_OPT_ADAMW ? segs[0].exp_avg_sq : nullptr;
+        sp.n = plan.numel;
+        sp.tile_word = reinterpret_cast<const uint32_t*>(base + L.words);
+        sp.change = reinterpret_cast<const uint32_t*>(base + L.changes);
+        sp.ntiles = (uint32_t)(plan.tile_word.size() - 1);
+    } else {
+        sl.chunks = reinterpret_cast<const Chunk*>(base + L.table);
+        sl.nchunks = (uint32_t)plan.table.size();
+    }
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
 
     DeviceScratch& d = g_dev[device];
     std::lock_guard<std::mutex> hold(d.busy);
-    // Every region the kernels read is written by this copy, and the partials are written
-    // by the norm pass before the finalize reads them: nothing depends on what an earlier
-    // call left in scratch.
+    // Every region the kernels read is written by this copy (the snapshot by the norm
+    // pass, the partials by the norm pass, both before they are read): nothing depends on
+    // what an earlier call left in scratch.
     e = hipMemcpyAsync(base, img.data(), L.end, hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess)
-        e = launch_norm(cfg->dtype, d_norm, nnorm, nb, d_state, d_partial, lds.norm, stream);
-    if (e == hipSuccess) e = launch_finalize(d_partial, nb, d_state, fa, stream);
-    if (e == hipSuccess) {
-        if (plan.flat) {
-            FlatSpan sp{};
-            sp.grad = static_cast<const uint16_t*>(segs[0].grad);
-            sp.half = static_cast<uint16_t*>(segs[0].half);
-            sp.master = segs[0].master;
-            sp.m = segs[0].exp_avg;
-            sp.v = cfg->optimizer == NEOX_OPT_ADAMW ? segs[0].exp_avg_sq : nullptr;
-            sp.n = plan.numel;
-            sp.tile_word = reinterpret_cast<const uint32_t*>(base + L.words);
-            sp.change = reinterpret_cast<const uint32_t*>(base + L.changes);
-            sp.ntiles = (uint32_t)(plan.tile_word.size() - 1);
-            e = launch_flat_update(cfg->dtype, cfg->optimizer, sp, d_state, ua, lds.flat, stream);
-        } else {
-            e = launch_update(cfg->dtype, cfg->optimizer, reinterpret_cast<const Chunk*>(base + L.table),
-                              (uint32_t)plan.table.size(), d_state, ua, lds.update, stream);
-        }
-    }
+    if (e == hipSuccess) e = enqueue_step(sl, lr, stream, nullptr);
     DevState st{};
     if (e == hipSuccess) e = hipMemcpyAsync(&st, d_state, sizeof st, hipMemcpyDeviceToHost, stream);
     // the upload image and the state copy must outlive the stream's use of them

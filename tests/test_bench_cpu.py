@@ -117,7 +117,7 @@ def test_summaries_record_extra_bench_flags(tmp_path):
     args.bench_flags = "--chunked-update"
     bench.summarize_pmc(args)
     head = [ln for ln in (tmp_path / "s.txt").read_text().splitlines() if ln.startswith("#")]
-    assert any("--skip-steps 0 --chunked-update" in ln for ln in head)
+    assert any("--no-extra-workloads --chunked-update" in ln for ln in head)
     assert any("--bench-flags='--chunked-update'" in ln for ln in head)
     d = tmp_path / "trace"
     d.mkdir()
@@ -133,7 +133,8 @@ def test_summaries_record_extra_bench_flags(tmp_path):
                                              trace_steps=10, bench_log=None, out=str(out),
                                              bench_flags="--chunked-update"))
     text = out.read_text()
-    assert "--steps 10 --warmup 3 --no-cpu-baseline --skip-steps 0 --chunked-update" in text
+    assert ("--steps 10 --warmup 3 --no-cpu-baseline --skip-steps 0 --no-ceiling "
+            "--no-extra-workloads --chunked-update") in text
     assert "+ 10 steps" in text and "--trace-steps 10" in text
 
 
@@ -200,3 +201,53 @@ def test_skipped_step_timing_restores_the_gradient(monkeypatch):
     lib = FakeLib(skips=False)
     with pytest.raises(AssertionError):
         bench.time_skipped_steps(lib, 0, grad, make_step(lib), 3, events=False)
+
+
+def test_stall_summary_table(tmp_path):
+    """bench.summarize_stalls: per-kernel averages of the memory-side counters, turned into
+    the duration, effective clock, latencies (LEVEL / REQ), requests in flight (LEVEL /
+    cycles) and credit-stall percentages the table reports; torch kernels are left out."""
+    upd = "void nz1::flat_update_kernel<1, 0>(nz1::FlatSpan, unsigned int const*)"
+    cpy = "void (anonymous namespace)::copy_kernel<true>(unsigned int __vector(4) const*)"
+    torch_k = "void at::native::vectorized_elementwise_kernel<4, at::native::float16_copy_kernel_cuda>()"
+    vals = {  # per dispatch
+        upd: dict(GRBM_GUI_ACTIVE=8 * 2_000_000, TCC_EA0_RDREQ_sum=1000, TCC_EA0_RDREQ_LEVEL_sum=2_000_000,
+                  TCC_EA0_WRREQ_sum=500, TCC_EA0_WRREQ_LEVEL_sum=250_000,
+                  TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum=128 * 20_000,
+                  TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum=128 * 40_000,
+                  TCP_TCC_READ_REQ_LATENCY_sum=3000, TCP_TCC_READ_REQ_sum=10,
+                  TCC_HIT_sum=3, TCC_MISS_sum=1),
+        cpy: dict(GRBM_GUI_ACTIVE=8 * 500_000, TCC_EA0_RDREQ_sum=10, TCC_EA0_RDREQ_LEVEL_sum=50,
+                  TCC_EA0_WRREQ_sum=10, TCC_EA0_WRREQ_LEVEL_sum=20,
+                  TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum=0, TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum=0,
+                  TCP_TCC_READ_REQ_LATENCY_sum=100, TCP_TCC_READ_REQ_sum=1, TCC_HIT_sum=1, TCC_MISS_sum=1),
+        torch_k: dict(GRBM_GUI_ACTIVE=1.0),
+    }
+    d = tmp_path / "stalls" / "p1"
+    d.mkdir(parents=True)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for k, cs in vals.items():
+            dur = 1_000_000 if k == upd else 200_000           # ns: 2.0 and 2.5 GHz
+            for c, v in cs.items():
+                w.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v,
+                            "Start_Timestamp": 10, "End_Timestamp": 10 + dur})
+    with open(d / "run_agent_info.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Agent_Type", "Num_Xcc"])
+        w.writeheader()
+        w.writerow({"Agent_Type": "CPU", "Num_Xcc": 1})
+        w.writerow({"Agent_Type": "GPU", "Num_Xcc": 8})
+    out = tmp_path / "stalls.txt"
+    bench.summarize_stalls(argparse.Namespace(stalls=str(tmp_path / "stalls"),
+                                              workload="neox20b_shard_215m", out=str(out)))
+    rows = {ln.split()[0]: ln.split() for ln in out.read_text().splitlines()
+            if ln.startswith(("nz1::", "copy_kernel"))}
+    assert set(rows) == {"nz1::flat_update_kernel<1,", "copy_kernel<true>"}
+    u = rows["nz1::flat_update_kernel<1,"][2:]          # after the split name
+    # n, us, GHz, rd_req, wr_req, rd_lat, rd_infl, wr_lat, wr_infl, rdstl%, wrstl%, tcp, hit
+    assert u[0] == "1" and float(u[1]) == 1000.0 and float(u[2]) == 2.0
+    assert float(u[5]) == 2000 and float(u[6]) == 1 and float(u[7]) == 500
+    assert float(u[9]) == 1.0 and float(u[10]) == 2.0 and float(u[11]) == 300 and float(u[12]) == 75.0
+    assert "GRBM_GUI_ACTIVE" in out.read_text() and "rocprofv3 --pmc" in out.read_text()

@@ -27,9 +27,14 @@ def _outputs(shard):
 # split step
 # ----------------------------------------------------------------------------------
 
-def test_split_step_equals_step_on_one_rank():
-    """step == step_local followed by step_apply on the local value, bit for bit."""
-    w = _custom("split1", [70_001, 4096, 33], [True, False, True], clip_norm=0.05)
+@pytest.mark.parametrize("sizes", [[70_001, 4096, 33], [3000] * 150, [1000] * 256],
+                         ids=["38_parts", "150_parts", "256_parts"])
+def test_split_step_equals_step_on_one_rank(sizes):
+    """step == step_local followed by step_apply on the local value, bit for bit.  These
+    shards' norm passes have at most 256 blocks, so the step's update takes the decisions
+    itself while the split step's finalize takes them: the two must agree bit for bit,
+    whether the partials fill one wave of the finalize or all four."""
+    w = _custom("split1", sizes, [k % 3 != 1 for k in range(len(sizes))], clip_norm=0.05)
     w.injections = {2: [(10, "nan")]}
     stream = torch.cuda.current_stream().cuda_stream
     outs, states = [], []
@@ -37,6 +42,8 @@ def test_split_step_equals_step_on_one_rank():
         sh = DeviceShard(w)
         sh.init_()
         h = Z.neox_zero1_create(lib_config(w), sh.neox_segments(), stream)
+        plan, _, _, _ = Z.neox_zero1_plan(lib_config(w), sh.neox_segments(), tables=False)
+        assert plan.norm_chunks <= 256, plan.norm_chunks
         loc = torch.zeros(1, dtype=torch.float64, device="cuda")
         st_seq = []
         for k in range(5):
@@ -385,7 +392,8 @@ def test_timing_events_record_and_change_nothing():
     count the steps they cover (up to max_steps), report positive durations that fit in
     the wall-clock time of those steps, and a new begin discards an unfinished one."""
     import time
-    w = _custom("timing", [3_000_000, 7, 1_000_001], [True, False, True])
+    # over 256 norm chunks, so the finalize is its own launch
+    w = _custom("timing", [9_000_000, 7, 1_000_001], [True, False, True])
     stream = torch.cuda.current_stream().cuda_stream
     a, b = DeviceShard(w), DeviceShard(w)
     a.init_()
@@ -423,6 +431,22 @@ def test_timing_events_record_and_change_nothing():
         assert len(per) == 2 and abs(sum(per) - sums[2]) <= 1e-6 * sums[2] + 1e-9, (per, sums)
         sa, sb = Z.neox_scaler_state(ha), Z.neox_scaler_state(hb)
         assert sa.step == sb.step == 7 and sa.last_sumsq == sb.last_sumsq
+        # a shard whose norm pass has at most 256 blocks: the update takes the decisions
+        # itself, no finalize is launched and its time reads 0
+        small = DeviceShard(_custom("timing_small", [40_000, 3], [True, False]))
+        small.init_()
+        small.grads_(0, 65536.0)
+        hs = Z.neox_zero1_create(lib_config(small.w), small.neox_segments(), stream)
+        try:
+            Z.neox_zero1_timing_begin(hs, 2)
+            Z.neox_zero1_step(hs, 1e-3, stream)
+            Z.neox_zero1_step(hs, 1e-3, stream)
+            sums, n, per = Z.neox_zero1_timing_end(hs, per_step=2)
+            assert n == 2 and sums[0] > 0.0 and sums[1] == 0.0 and sums[2] > 0.0, sums
+            assert len(per) == 2 and sum(per) >= sums[0] + sums[2] - 1e-6, (per, sums)
+            assert Z.neox_scaler_state(hs).step == 2
+        finally:
+            Z.neox_zero1_destroy(hs)
         oa, ob = _outputs(a), _outputs(b)
         for k in oa:
             assert torch.equal(oa[k], ob[k]), k

@@ -87,6 +87,6 @@ def test_pythia410m_layout():
     assert len(segs1) == 36
     assert sum(s["numel"] for s in segs1 if not s["flags"]) == 38_912
     for r in range(8):
-        w = workloads.pythia410m(r)
         segs, _ = O.partition(numel, decay, 8, r, 64)
-        assert [(s["numel"], bool(s["flags"])) for s in segs] == list(w.segments)
+        w = workloads.pythia410m(r, [(s["numel"], s["flags"]) for s in segs])
+        assert w.numel == P and w.name == f"pythia410m_dp8_rank{r}"

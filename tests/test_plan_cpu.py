@@ -132,9 +132,11 @@ def test_chunk_table_bruteforce(chunk):
         C = chunk or plan.chunk_elems
         assert as_tuples(chunks) == expected_chunks(segs, C), (case, sizes)
         assert plan.update_chunks == len(chunks) and plan.numel == sum(sizes)
-        # norm chunks: the smallest multiple of C that is at least the default norm length
+        # norm chunks: the smallest multiple of C that is at least the default norm length,
+        # or, on a shard under 64 of those, at least numel / 64 (and at least C)
         C1 = plan.norm_chunk_elems
-        assert C1 % C == 0 and C1 >= 32768 and C1 - C < 32768
+        target = min(32768, max(C, -(-sum(sizes) // 64)))
+        assert C1 % C == 0 and C1 >= target and C1 - C < target
         assert plan.norm_chunks == len(expected_chunks(segs, C1))
 
 
@@ -160,7 +162,9 @@ def test_flat_tile_table_rebuilds_every_decay_flag(seed):
 def test_plan_of_benchmark_shards():
     """The GPT-NeoX-20B per-rank shard and a Pythia-410M rank as flat partitions: tile
     count, flag changes inside tiles and chunk counts follow from the segment list."""
-    for w in (W.neox20b_shard(), W.pythia410m(1)):
+    t = W.pythia410m_tensors()
+    psegs, _ = Z.neox_zero1_partition([n for n, _ in t], [d for _, d in t], 8, 1, 64)
+    for w in (W.neox20b_shard(), W.pythia410m(1, [(s.numel, s.flags) for s in psegs])):
         sizes = [n for n, _ in w.segments]
         decays = [d for _, d in w.segments]
         segs = flat_segments(sizes, decays)

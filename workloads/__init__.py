@@ -124,25 +124,14 @@ def tiny() -> Workload:
                     injections={5: [(777_777, "+inf")]})
 
 
-def pythia410m(rank: int = 0, dp: int = 8, steps: int = 20) -> Workload:
+def pythia410m(rank: int, segments, dp: int = 8, steps: int = 20) -> Workload:
     """Rank `rank` of a DP=`dp` ZeRO-1 partition of the Pythia-410M-like tensor list.
 
-    The segment list is the intersection of each tensor with the rank's range of the
-    flat concat (the partition itself is computed by the code under test / the oracle;
-    here it is written out only to size the buffers)."""
-    tensors = pythia410m_tensors()
-    total = sum(n for n, _ in tensors)
-    unit = dp * 64
-    padded = -(-total // unit) * unit
-    P = padded // dp
-    lo, hi = rank * P, (rank + 1) * P
-    segs, off = [], 0
-    for n, d in tensors + [(padded - total, False)]:
-        a, b = max(off, lo), min(off + n, hi)
-        if a < b:
-            segs.append((b - a, d))
-        off += n
-    return Workload(f"pythia410m_dp{dp}_rank{rank}", 2, segs, Hyper(), steps=steps)
+    segments: the rank's [(numel, decay)] in shard order, as a partition of
+    pythia410m_tensors() gives them (the library's for the GPU side, the oracle's for the
+    oracle side): this module only sizes and seeds the buffers, it does not partition."""
+    return Workload(f"pythia410m_dp{dp}_rank{rank}", 2, [(int(n), bool(d)) for n, d in segments],
+                    Hyper(), steps=steps)
 
 
 def neox20b_shard(steps: int = 100) -> Workload:
@@ -197,11 +186,11 @@ def opt_large(numel: int = 6_000_000_000) -> Workload:
                     injections=inj)
 
 
+# Workloads that need no partition; the Pythia-410M ranks are built from a partition by
+# the caller (pythia410m).
 BENCH_WORKLOADS = {
     "neox20b_shard_215m": neox20b_shard,
     "tiny_1m": tiny,
-    "pythia410m_dp8_rank0": lambda: pythia410m(0),
-    "pythia410m_dp8_rank1": lambda: pythia410m(1),
     "multi_tensor_5000_bf16": multi_tensor,
     "multi_tensor_5000_bf16_literal": lambda: multi_tensor(literal=True),
     "opt_style_6b": opt_large,
