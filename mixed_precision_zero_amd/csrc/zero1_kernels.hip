@@ -447,22 +447,51 @@ struct Fuse {
     DevState* st;                // written by block 0
     FinalizeArgs fin;
 };
-__device__ __forceinline__ Decision fused_decide(const Fuse& f) {
+// The loads of fused_decide, so that a caller can issue them ahead of its data loads and
+// let the decision's arithmetic overlap the data's latency.
+struct FusedIn {
+    double p[kFinalizeBlock / 64];   // this lane's partial of each finalize wave (0 if none)
+    PreState pre;
+};
+__device__ __forceinline__ FusedIn fused_load(const Fuse& f) {
+    const uint32_t lane = threadIdx.x & 63;
+    FusedIn in;
+    // unconditional loads (a lane past the partials reads partial[0], which fused_finish
+    // ignores), so they issue back to back without a wait between them
+#pragma unroll
+    for (int w = 0; w < kFinalizeBlock / 64; ++w) {
+        const uint32_t i = w * 64 + lane;
+        in.p[w] = f.partial[i < f.nparts ? i : 0];
+    }
+    in.pre = read_pre(f.snap);
+    return in;
+}
+// Issued after a block's data loads: the decision's arithmetic cannot be scheduled above
+// this point (it depends on the values passed through), and the data loads cannot sink
+// below it, so the arithmetic overlaps the data's latency.  Register operands only.
+__device__ __forceinline__ void after_data(FusedIn& in) {
+    static_assert(kFinalizeBlock / 64 == 4, "four partial registers");
+    asm volatile("" : "+v"(in.p[0]), "+v"(in.p[1]), "+v"(in.p[2]), "+v"(in.p[3]) : : "memory");
+}
+__device__ __forceinline__ Decision fused_finish(const FusedIn& in, const Fuse& f) {
     const uint32_t lane = threadIdx.x & 63;
     // finalize waves holding partials; the others sum to +0, which is added as such
     const uint32_t waves = (f.nparts + 63) / 64;
     double r = 0.0;
+#pragma unroll
     for (uint32_t w = 0; w < kFinalizeBlock / 64; ++w) {
         double v = 0.0;
         if (w < waves) {
-            const uint32_t i = w * 64 + lane;
-            if (i < f.nparts) v = 0.0 + f.partial[i];
+            if (w * 64 + lane < f.nparts) v = 0.0 + in.p[w];
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
         }
         r = w == 0 ? v : r + v;
     }
-    return decide(r, read_pre(f.snap), f.fin);
+    return decide(r, in.pre, f.fin);
+}
+__device__ __forceinline__ Decision fused_decide(const Fuse& f) {
+    return fused_finish(fused_load(f), f);
 }
 
 // ------------------------------------------------------------------------------------
@@ -741,9 +770,10 @@ __device__ __forceinline__ StepWords ld_after(const DevState* st, const uint32_t
 // behind the data (ld_after), or, with FUSE, taken by the block itself (block 0 also
 // writes the state block).
 template <bool FUSE>
-__device__ __forceinline__ StepWords step_words(const DevState* st, const uint32_t* word, const Fuse& f) {
+__device__ __forceinline__ StepWords step_words(const DevState* st, const uint32_t* word, const Fuse& f,
+                                                const FusedIn& in) {
     if constexpr (FUSE) {
-        const Decision d = fused_decide(f);
+        const Decision d = fused_finish(in, f);
         if (blockIdx.x == 0 && threadIdx.x == 0) write_state(f.st, d.next);
         StepWords r;
         r.skip = d.next.skip;
@@ -790,6 +820,10 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
         if (st->skip | (int32_t)low) return;
     }
 #endif
+    // With FUSE the decision's inputs are loaded first, so its arithmetic overlaps the
+    // data loads' latency.
+    FusedIn fin_in{};
+    if constexpr (FUSE) fin_in = fused_load(f);
     if (T + 1 < s.ntiles || s.n % kFlatTile == 0) {
         // a full tile: every thread owns U whole vectors
         uint4 G[U];
@@ -798,8 +832,9 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
         for (int u = 0; u < U; ++u)
             load8<OPT>(g4, w4, m4, v4, v0 + u * kFlatBlock + threadIdx.x, G[u], W[u], M[u], V[u]);
         // Then the decision, the coefficients and the tile words, as vector loads issued
-        // behind the data (see ld_after).
-        const StepWords sw = step_words<FUSE>(st, tile_word + T, f);
+        // behind the data (see ld_after), or the block's own decision (FUSE).
+        if constexpr (FUSE) after_data(fin_in);
+        const StepWords sw = step_words<FUSE>(st, tile_word + T, f, fin_in);
         const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
         const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
         const uint32_t start_mask = (sw.w0 & 1u) ? 0xFFu : 0u;
@@ -830,7 +865,7 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
 
     // the last tile, shorter than kFlatTile: guarded vectors, then the last n % 8
     // elements on the scalar path
-    const StepWords sw = step_words<FUSE>(st, tile_word + T, f);
+    const StepWords sw = step_words<FUSE>(st, tile_word + T, f, fin_in);
     if (sw.skip) return;
     const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
     const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
