@@ -1,5 +1,6 @@
 """neox_zero1_step_noalloc (the entry point for callers that cannot allocate device
-memory) against neox_zero1_step on identical inputs, through the C ABI.
+memory) against neox_zero1_step on identical inputs, through the C ABI.  (Named to be
+collected last: the GPU suite runs with -x.)
 
 Both run the same kernels, so every array and every scaler field must agree bit for bit.
 Two calls in a row, the second on a smaller input with another layout: a flat fp16
@@ -105,3 +106,30 @@ def test_noalloc_equals_step_two_calls_second_smaller():
     st = _run_pair(small, 2, flat=False, misalign=(1, 2, 1, 3, 1), oracle_check=False)
     assert (st.step, st.skipped_total) == (2, 0)
 
+
+
+def test_noalloc_equals_step_with_a_separate_finalize_and_sgd():
+    """A 9M-element flat shard, whose norm pass has more than 256 blocks so the step runs
+    its separate finalize launch (the first test's shards take the decision in the
+    update), checked against the oracle too; then a smaller momentum-SGD shard in
+    separate allocations."""
+    sizes = [6_000_000, 7, 3_000_001]
+    big = W.Workload("noalloc_flat_9m", 73, [(n, k != 1) for k, n in enumerate(sizes)], W.Hyper(),
+                     steps=2)
+    base, off, fake = 1 << 36, 0, []
+    for n in sizes:               # addresses of a flat layout, only compared by the plan
+        fake.append(Z.neox_segment(base + 2 * off, base + (1 << 34) + 2 * off,
+                                   base + 2 * (1 << 34) + 4 * off, base + 3 * (1 << 34) + 4 * off,
+                                   base + 4 * (1 << 34) + 4 * off, n, 1, 0, 0))
+        off += n
+    plan, _, _, _ = Z.neox_zero1_plan(lib_config(big), fake, tables=False)
+    assert plan.norm_chunks > 256, plan.norm_chunks
+    log(f"case noalloc flat 9M: {big.numel} elements, {plan.norm_chunks} norm chunks")
+    st = _run_pair(big, 2, flat=True, misalign=(0, 0, 0, 0, 0), oracle_check=True)
+    assert (st.step, st.skipped_total) == (2, 0)
+
+    sgd = W.Workload("noalloc_sep_sgd", 74, [(30_000, True), (1_001, False)],
+                     W.Hyper(optimizer=1), steps=3, injections={1: [(7, "nan")]})
+    log(f"case noalloc separate sgd: {sgd.numel} elements")
+    st = _run_pair(sgd, 3, flat=False, misalign=(1, 0, 1, 2, 0), oracle_check=True)
+    assert (st.step, st.skipped_total) == (2, 1)
