@@ -336,8 +336,9 @@ int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint
                     uint32_t* tile_words, uint64_t word_cap, uint32_t* changes,
                     uint64_t change_cap);
 
-/* For callers that cannot allocate device memory (code under HIP graph capture, tight
- * serving loops, harnesses that forbid hipMalloc): one whole step -- the same kernels and
+/* For callers that cannot allocate device memory (tight serving loops, harnesses that
+ * forbid hipMalloc; the call synchronizes its stream, so it is not one to record inside
+ * a HIP graph capture): one whole step -- the same kernels and
  * launch shapes as neox_zero1_step, so the same bits for the same inputs -- with no
  * handle and no device allocation.  cfg and segs[nseg] are as for neox_zero1_create
  * (host memory; segment_norms must be 0).  *state (host) is read for the scaler state

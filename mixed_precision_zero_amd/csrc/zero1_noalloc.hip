@@ -1,7 +1,8 @@
 // zero1_noalloc.hip -- neox_zero1_step_noalloc: one step of the ZeRO-1 mixed-precision
 // Adam update with no handle and no device allocation, for callers that cannot allocate
-// device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
-// hipMalloc).
+// device memory (tight serving loops, harnesses that forbid hipMalloc).  It uploads its
+// tables and reads the state back with a stream synchronization, so it is not a call to
+// record inside a HIP graph capture.
 //
 // Everything the step's kernels need besides the caller's arrays -- the device state
 // block, the norm pass's per-block partial sums and the work tables -- lives in one
