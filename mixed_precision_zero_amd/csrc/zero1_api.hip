@@ -42,7 +42,8 @@ int set_hip_error(hipError_t e, const char* what) {
 namespace {
 
 // Work-unit sizes (elements), measured best on MI355X: the update wants small blocks
-// (2,048 elements: 128 threads x two 16-byte vectors per array) at 2 blocks per CU, the
+// (2,048 elements: 128 threads x two 16-byte vectors per array) at 2 blocks per CU on
+// long grids, the
 // read-only norm pass more bytes per block (32K elements, 8 loads in flight per thread)
 // at 4 blocks per CU.
 #ifndef NZ1_UPDATE_CHUNK
@@ -67,6 +68,22 @@ namespace {
 // momentum SGD moves 20 B/param over seven streams and prefers more blocks in flight
 #ifndef NZ1_FLAT_BLOCKS_PER_CU_SGD
 #define NZ1_FLAT_BLOCKS_PER_CU_SGD 4
+#endif
+// Short update grids want more blocks in flight: a pass of a few blocks per CU is
+// dominated by its ramp-up and drain, while on long grids more tiles in flight mean more
+// open DRAM rows.  Up to NZ1_SMALL_GRID blocks per CU of grid the AdamW update runs 4
+// blocks per CU, up to NZ1_MID_GRID 8, beyond that the defaults above.  Measured on MI355X,
+// flat shards, us per step at 2 / 4 / 8 blocks per CU: 2M elements 18.5 / 15.9 / 15.9,
+// 8M 50.8 / 47.5 / 48.3, 16M 90.8 / 86.6 / 84.4, 20M 111.3 / 106.9 / 104.9, 24M
+// 125.7 / 127.4 / 125.4, 32M 171.5 / 180.1 / 185.1, 44M 239.7 / 246.3 / 255.0 (on 256
+// CUs the grid has 4 blocks per CU at 2M, 15 at 8M, 38 at 20M, 46 at 24M; M = 1e6
+// elements); the chunk-table update follows
+// the same curve (8M 66.3 / 53.0 / 52.8, 16M 95.8 / 91.4 / 91.5, 32M 177.5 / 181.0 / 187.5).
+#ifndef NZ1_SMALL_GRID
+#define NZ1_SMALL_GRID 16
+#endif
+#ifndef NZ1_MID_GRID
+#define NZ1_MID_GRID 40
 #endif
 // Timing events skip the system-scope fence an event otherwise performs when it
 // completes (an L2 write-back and invalidate that slows the kernels after it): they are
@@ -500,19 +517,35 @@ static uint32_t reserve_for(int lds_per_cu, uint32_t per_cu, uint32_t fixed) {
     return total > fixed ? total - fixed : 0u;
 }
 
-int lds_reserve(int device, int optimizer, LdsReserve* out) {
-    int lds_per_cu = 0;
+// Blocks per CU for an update grid of `blocks` blocks on `cus` CUs.
+static uint32_t update_per_cu(uint64_t blocks, int cus, uint32_t long_grid) {
+    const uint64_t per = (blocks + (uint64_t)cus - 1) / (uint64_t)cus;
+    if (per <= NZ1_SMALL_GRID) return long_grid > 4u ? long_grid : 4u;
+    if (per <= NZ1_MID_GRID) return long_grid > 8u ? long_grid : 8u;
+    return long_grid;
+}
+
+int lds_reserve(int device, int optimizer, uint64_t update_blocks, LdsReserve* out) {
+    int lds_per_cu = 0, cus = 0;
     hipError_t e = hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
                                          device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
     if (e != hipSuccess) return set_hip_error(e, "hipDeviceGetAttribute");
+    if (cus < 1) cus = 1;
     uint32_t norm_fixed = 0;
     e = norm_static_lds(&norm_fixed);
     if (e != hipSuccess) return set_hip_error(e, "hipFuncGetAttributes");
     out->norm = reserve_for(lds_per_cu, NZ1_NORM_BLOCKS_PER_CU, norm_fixed);
     // the update kernels declare no static LDS
-    out->update = reserve_for(lds_per_cu, NZ1_UPDATE_BLOCKS_PER_CU, 0);
-    out->flat = reserve_for(lds_per_cu, optimizer == NEOX_OPT_SGD ? NZ1_FLAT_BLOCKS_PER_CU_SGD
-                                                                 : NZ1_FLAT_BLOCKS_PER_CU, 0);
+    if (optimizer == NEOX_OPT_SGD) {
+        // momentum SGD keeps its fixed shapes: 8 per CU measured slower at every size
+        // (16M elements 66.8 against 64.5 us at 4 per CU)
+        out->update = reserve_for(lds_per_cu, NZ1_UPDATE_BLOCKS_PER_CU, 0);
+        out->flat = reserve_for(lds_per_cu, NZ1_FLAT_BLOCKS_PER_CU_SGD, 0);
+    } else {
+        out->update = reserve_for(lds_per_cu, update_per_cu(update_blocks, cus, NZ1_UPDATE_BLOCKS_PER_CU), 0);
+        out->flat = reserve_for(lds_per_cu, update_per_cu(update_blocks, cus, NZ1_FLAT_BLOCKS_PER_CU), 0);
+    }
     return NEOX_OK;
 }
 
@@ -576,7 +609,8 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) { free_handle(h); return set_hip_error(e, "hipGetDevice"); }
-    int rc2 = lds_reserve(h->device, cfg->optimizer, &sl.lds);
+    int rc2 = lds_reserve(h->device, cfg->optimizer,
+                          flat ? (uint64_t)tile_word.size() - 1 : (uint64_t)table.size(), &sl.lds);
     if (rc2) { free_handle(h); return rc2; }
     const uint32_t nnorm = (uint32_t)norm_table.size();
     // norm pass: one block per norm chunk unless a smaller striding grid is requested

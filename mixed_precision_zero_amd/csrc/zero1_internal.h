@@ -58,9 +58,10 @@ static_assert(offsetof(DevState, skip) % 16 == 0, "update fields share one 16-by
 
 // Flat layout: the segments, in order, tile five contiguous arrays whose first elements
 // are 16-byte aligned.  Work unit: one tile of kFlatTile elements per block.  Measured
-// best on MI355X: 128 threads x 2 vectors (2,048-element tiles) at 2 blocks per CU;
-// fewer tiles in flight per CU keep the chip's open DRAM rows few, and the block's
-// single round trip keeps that low occupancy from exposing latency.
+// best on MI355X: 128 threads x 2 vectors (2,048-element tiles) at 2 blocks per CU on
+// long grids; fewer tiles in flight per CU keep the chip's open DRAM rows few, and the
+// block's single round trip keeps that low occupancy from exposing latency.  (Grids of
+// up to 40 blocks per CU run 4 or 8 blocks per CU instead; see lds_reserve.)
 #ifndef NZ1_FLAT_BLOCK
 #define NZ1_FLAT_BLOCK 128
 #endif
@@ -208,7 +209,9 @@ DevState initial_state(const neox_zero1_config& cfg, float scale, int32_t good_s
 struct LdsReserve {
     uint32_t norm = 0, update = 0, flat = 0;
 };
-int lds_reserve(int device, int optimizer, LdsReserve* out);
+// update_blocks: the update grid (flat tiles or chunk-table entries), which sets how many
+// update blocks share a CU.
+int lds_reserve(int device, int optimizer, uint64_t update_blocks, LdsReserve* out);
 
 // Everything one step launches, with device addresses resolved: what a handle keeps and
 // what the allocation-free entry point assembles in its scratch.

@@ -112,7 +112,9 @@ extern "C" int neox_zero1_step_noalloc(const neox_zero1_config* cfg, const neox_
     rc = device_scratch(device, &base);
     if (rc) return rc;
     LdsReserve lds;
-    rc = lds_reserve(device, cfg->optimizer, &lds);
+    rc = lds_reserve(device, cfg->optimizer,
+                     plan.flat ? (uint64_t)plan.tile_word.size() - 1 : (uint64_t)plan.table.size(),
+                     &lds);
     if (rc) return rc;
 
     // Host image of everything the kernels read from scratch, uploaded in one copy.
