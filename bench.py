@@ -426,11 +426,23 @@ def host_info():
 CPU_THREADS_MAX = 16
 
 
+def _oracle_config(w):
+    """The oracle's configuration and initial scaler for workload w."""
+    from oracle import oracle as O
+    h = w.hyper
+    cfg = O.Config(beta1=h.beta1, beta2=h.beta2, eps=h.eps, weight_decay=h.weight_decay,
+                   clip_norm=h.clip_norm, predivide_factor=h.predivide_factor,
+                   dp_world_size=h.dp_world_size, dtype=h.dtype, scaler_mode=h.scaler_mode,
+                   growth_interval=h.growth_interval, growth_factor=h.growth_factor,
+                   backoff_factor=h.backoff_factor, min_scale=h.min_scale,
+                   optimizer=h.optimizer)
+    return cfg, O.Scaler(loss_scale=h.init_scale)
+
+
 def _oracle_setup(w, n=None):
     """Host inputs of workload w (its first n params) for the oracle: config, scaler and
     the segment list over freshly drawn arrays (the step-0 gradient)."""
     import workloads as W
-    from oracle import oracle as O
 
     n = w.numel if n is None else min(n, w.numel)
     segs, left = [], n
@@ -442,19 +454,14 @@ def _oracle_setup(w, n=None):
     st0 = W.host_init(w, n=n)
     g = W.host_grads(w, 0, w.hyper.init_scale, n=n)
     h = w.hyper
-    cfg = O.Config(beta1=h.beta1, beta2=h.beta2, eps=h.eps, weight_decay=h.weight_decay,
-                   clip_norm=h.clip_norm, predivide_factor=h.predivide_factor,
-                   dp_world_size=h.dp_world_size, dtype=h.dtype, scaler_mode=h.scaler_mode,
-                   growth_interval=h.growth_interval, growth_factor=h.growth_factor,
-                   backoff_factor=h.backoff_factor, min_scale=h.min_scale,
-                   optimizer=h.optimizer)
+    cfg, scaler = _oracle_config(w)
     osegs, off = [], 0
     for k, d in segs:
         sl = slice(off, off + k)
         osegs.append(dict(grad=g[sl], half=st0["half"][sl], master=st0["master"][sl],
                           m=st0["m"][sl], v=None if h.optimizer else st0["v"][sl], decay=d))
         off += k
-    return cfg, O.Scaler(loss_scale=h.init_scale), osegs, n
+    return cfg, scaler, osegs, n
 
 
 def _time_oracle(cfg, st, segs, n, threads, budget_s, max_steps):
@@ -477,10 +484,12 @@ def _time_oracle(cfg, st, segs, n, threads, budget_s, max_steps):
     return n * steps / spent, steps, spent
 
 
-def cpu_baseline(w, budget_s=10.0):
+def cpu_baseline(w, budget_s=10.0, dev=None):
     """The CPU oracle on this host: the bench workload in full, on all the cores this
     process may use (up to the box's share) and on one thread, plus the two small
-    workloads on all cores.  Same seeded inputs as the GPU side (host draws)."""
+    workloads on all cores; with dev, also the two large workloads (the 5,000-tensor
+    shard in full, the 6e9 shard windowed), their inputs drawn on that device.  Inputs
+    follow each workload's recipe (seeded host draws unless stated)."""
     info = host_info()
     threads = max(1, min(CPU_THREADS_MAX, info["affinity_cpus"]))
     cfg, st, segs, n = _oracle_setup(w)
@@ -495,6 +504,15 @@ def cpu_baseline(w, budget_s=10.0):
         r, ns, sec = _time_oracle(c, s2, sg, k, threads, 1.0, 20)
         small[name] = {"value": r, "params": k, "steps": ns, "seconds": round(sec, 2),
                        "cores": threads}
+    large = {}
+    if dev is not None:
+        for name, fn in (("multi_tensor_5000_bf16", cpu_multi_tensor_in_full),
+                         ("opt_style_6b", cpu_opt_style_windowed)):
+            print(f"[bench] cpu baseline (oracle): {name}", file=sys.stderr, flush=True)
+            try:
+                large[name] = fn(dev, threads)
+            except Exception as e:      # a reported baseline: never lose the bench line to it
+                large[name] = {"error": repr(e)}
     what = (f"{w.name} in full ({n} params, {len(w.segments)} segments), step-0 gradient; "
             f"all-core: {steps_t} steps on {threads} threads in {sec_t:.1f} s (static contiguous "
             f"pieces, per-thread double partial sums added in thread order); one thread: "
@@ -506,7 +524,169 @@ def cpu_baseline(w, budget_s=10.0):
                               "seconds": round(sec_1, 2),
                               "gbps": STEP_BYTES_PER_PARAM * rate_1 / 1e9},
             "other_workloads_in_full": small,
+            **({"large_workloads": large} if large else {}),
             "host": info}
+
+
+def _host_bits(t):
+    """Host (numpy) copy of a CUDA tensor; 16-bit formats as their uint16 bits."""
+    import numpy as np
+    import torch
+    a = t.cpu()
+    return a.view(torch.int16).numpy().view(np.uint16) if a.element_size() == 2 else a.numpy()
+
+
+def cpu_multi_tensor_in_full(dev, threads, budget_s=5.0):
+    """The oracle on all cores over the whole 5,000-tensor shard (1e9 params): the
+    step-0 inputs drawn by the workload's seeded device generators and copied to host
+    memory, then whole steps as for the bench workload."""
+    import gc
+
+    import torch
+    w = make_workload("multi_tensor_5000_bf16")
+    keep, _ = alloc_shard(w, dev, sgd=False)
+    segs = [dict(grad=_host_bits(a["grad"]), half=_host_bits(a["half"]),
+                 master=_host_bits(a["master"]), m=_host_bits(a["m"]), v=_host_bits(a["v"]),
+                 decay=decay) for a, (_, decay) in zip(keep, w.segments)]
+    del keep
+    gc.collect()
+    torch.cuda.empty_cache()
+    cfg, st = _oracle_config(w)
+    rate, steps, sec = _time_oracle(cfg, st, segs, w.numel, threads, budget_s, 3)
+    return {"value": rate, "unit": "params/s", "params": w.numel, "segments": len(w.segments),
+            "steps": steps, "seconds": round(sec, 2), "cores": threads,
+            "gbps": STEP_BYTES_PER_PARAM * rate / 1e9,
+            "sample": "in full: device-drawn step-0 inputs copied to host, whole steps on all "
+                      "cores (static contiguous pieces, thread-order partial sums)"}
+
+
+def windowed_runs(w, windows=64, win=1 << 20, edge=4096, seed=7):
+    """The elements the windowed CPU update covers: `windows` seeded windows of `win`
+    elements (each clipped to the end of the segment it starts in) and the first and last
+    `edge` elements of every segment.  Returns (start, length, decay) runs in shard order;
+    runs may overlap one another."""
+    import numpy as np
+    sizes = [k for k, _ in w.segments]
+    starts = np.concatenate([[0], np.cumsum(sizes)])
+    runs = []
+    for k, (n, d) in enumerate(w.segments):
+        s0 = int(starts[k])
+        if n <= 2 * edge:
+            runs.append((s0, n, d))
+        else:
+            runs.append((s0, edge, d))
+            runs.append((s0 + n - edge, edge, d))
+    rng = np.random.default_rng([w.wid, seed])
+    for a in rng.integers(0, max(1, w.numel - win), size=windows):
+        k = int(np.searchsorted(starts, a, side="right")) - 1
+        end = min(int(a) + win, int(starts[k + 1]))
+        runs.append((int(a), end - int(a), w.segments[k][1]))
+    return sorted(runs)
+
+
+def oracle_windowed_step(w, fetch, runs, threads, piece=1 << 28):
+    """One oracle step of workload w timed the windowed way: the squared norm over the
+    whole gradient, streamed through a host buffer `piece` elements at a time
+    (fetch(lo, k, out) fills out[:k] with the gradient's bits [lo, lo + k); each piece
+    is scanned on `threads` threads, partials added in thread order), one decision, then
+    the update of the given runs on `threads` threads.  fetch(lo, k) returns the
+    gradient's bits [lo, lo + k) as a uint16 array (k <= piece) that stays valid until the
+    next call.  Only the oracle's calls are timed.  Returns (scan seconds, update seconds,
+    updated params, decision, squared norm)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import oracle as O
+    cfg, st = _oracle_config(w)
+    inv, inv32 = O.unscale_factor(cfg, st)
+    n = w.numel
+    sumsq, of, scan_s = 0.0, 0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for lo in range(0, n, piece):
+            k = min(piece, n - lo)
+            buf = fetch(lo, k)
+            cut = [k * p // threads for p in range(threads + 1)]
+            t0 = time.perf_counter()
+            parts = list(ex.map(lambda p: O.scan(cfg.dtype, buf[cut[p]:cut[p + 1]], inv, inv32),
+                                range(threads)))
+            scan_s += time.perf_counter() - t0
+            for s_, o_ in parts:
+                sumsq += s_
+                of |= o_
+        d = O.decide(cfg, st, of, sumsq)
+        # the runs' inputs: the gradient from the shard, a fresh step-0 state of the
+        # workload's recipe (master ~ N(0, sigma), half = cast(master), m = v = 0)
+        rng = np.random.default_rng([w.wid, 8])
+        work = []
+        for a, k, decay in runs:
+            g = np.array(fetch(a, k), copy=True)
+            master = (rng.standard_normal(k) * w.master_sigma).astype(np.float32)
+            work.append(dict(grad=g, half=O.float_to_half(cfg.dtype, master), master=master,
+                             m=np.zeros(k, np.float32), v=np.zeros(k, np.float32), decay=decay))
+        # longest runs first, each to the least-loaded thread
+        groups, load = [[] for _ in range(threads)], [0] * threads
+        for r in sorted(work, key=lambda r: -r["grad"].size):
+            t = load.index(min(load))
+            groups[t].append(r)
+            load[t] += r["grad"].size
+        lr = np.float32(w.hyper.lr)
+
+        def update_group(group):
+            for r in group:
+                O.update(cfg, d, lr, r["grad"], r["half"], r["master"], r["m"], r["v"],
+                         r["decay"])
+
+        t0 = time.perf_counter()
+        list(ex.map(update_group, groups))
+        upd_s = time.perf_counter() - t0
+    return scan_s, upd_s, sum(k for _, k, _ in runs), d, sumsq
+
+
+def cpu_opt_style_windowed(dev, threads):
+    """The oracle on the 6e9-param OPT-style shard, windowed (its 108 GB of host arrays
+    and tens of minutes of single-core work are out of a bench run's reach): the norm over
+    the whole device-drawn step-0 gradient, the update on seeded windows, and the step
+    time estimated as norm time + update time scaled to the whole shard."""
+    import gc
+
+    import torch
+
+    import workloads as W
+    w = make_workload("opt_style_6b")
+    dt = torch.float16 if w.hyper.dtype == W.F16 else torch.bfloat16
+    grad = torch.empty(w.numel, dtype=dt, device=dev)
+    W.device_grads_(w, grad, 0, w.hyper.init_scale)
+    piece = min(1 << 28, w.numel)
+    pinned = torch.empty(piece, dtype=dt, pin_memory=True)
+    pinned_bits = pinned.view(torch.int16).numpy().view("uint16")
+
+    def fetch(lo, k):
+        pinned[:k].copy_(grad[lo:lo + k])      # synchronous device-to-host copy
+        return pinned_bits[:k]
+
+    runs = windowed_runs(w)
+    try:
+        scan_s, upd_s, n_upd, d, _ = oracle_windowed_step(w, fetch, runs, threads, piece)
+    finally:
+        del grad, pinned
+        gc.collect()
+        torch.cuda.empty_cache()
+    n = w.numel
+    est = scan_s + upd_s * n / n_upd
+    return {"value": n / est, "unit": "params/s", "params": n, "segments": len(w.segments),
+            "cores": threads, "windowed": True,
+            "norm_pass": {"params": n, "seconds": round(scan_s, 2),
+                          "params_per_s": n / scan_s},
+            "update": {"params": n_upd, "runs": len(runs), "seconds": round(upd_s, 3),
+                       "params_per_s": n_upd / upd_s},
+            "estimated_step_s": round(est, 2), "skipped": bool(d.skip),
+            "gbps": STEP_BYTES_PER_PARAM * n / est / 1e9,
+            "sample": "windowed: squared norm over the whole device-drawn step-0 gradient "
+                      "(copied to host in 2^28-element pieces, copies not timed), update on 64 "
+                      "seeded 1M-element windows plus every segment's first and last 4K "
+                      "elements; value = params / (norm time + update time scaled to the "
+                      "whole shard)"}
 
 
 def time_skipped_steps(Z, h, grad, one_step, steps, events):
@@ -692,6 +872,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="neox20b_shard_215m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-large", action="store_true",
+                    help="CPU baseline without the 5,000-tensor (in full) and 6e9 (windowed) "
+                         "shards")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the copy / access-pattern probes after the timed steps")
     ap.add_argument("--no-extra-workloads", action="store_true",
@@ -891,7 +1074,9 @@ def main():
                 out["workloads"][name] = extra_workload(name, dev, k, wu)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w)
+        large = (not args.no_extra_workloads and not args.no_cpu_large and
+                 "workloads" in out)
+        out["cpu_baseline"] = cpu_baseline(w, dev=dev if large else None)
     print(json.dumps(out), flush=True)
 
 

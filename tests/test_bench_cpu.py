@@ -251,3 +251,46 @@ def test_stall_summary_table(tmp_path):
     assert float(u[5]) == 2000 and float(u[6]) == 1 and float(u[7]) == 500
     assert float(u[9]) == 1.0 and float(u[10]) == 2.0 and float(u[11]) == 300 and float(u[12]) == 75.0
     assert "GRBM_GUI_ACTIVE" in out.read_text() and "rocprofv3 --pmc" in out.read_text()
+
+
+def test_windowed_cpu_baseline_covers_runs_and_the_whole_norm():
+    """The windowed CPU step (used for the 6e9 shard): every run lies inside one segment
+    with that segment's decay flag, every segment's ends are covered, and the squared
+    norm streamed piece by piece on several threads is the oracle's scan of the whole
+    gradient up to summation order."""
+    import numpy as np
+
+    import bench
+    import workloads as W
+    from oracle import oracle as O
+    w = W.Workload("windowed", 9, [(300_000, True), (5, False), (1_000_000, True),
+                                   (9_000, False)], W.Hyper(), steps=1)
+    g = W.host_grads(w, 0, w.hyper.init_scale)
+    runs = bench.windowed_runs(w, windows=6, win=50_000, edge=512)
+    starts = np.cumsum([0] + [k for k, _ in w.segments])
+    for a, k, d in runs:
+        seg = int(np.searchsorted(starts, a, side="right")) - 1
+        assert k >= 1 and a + k <= starts[seg + 1] and d == w.segments[seg][1]
+    covered = {(a, k) for a, k, _ in runs}
+    for s, (n, _) in zip(starts, w.segments):
+        if n <= 1024:
+            assert (int(s), n) in covered
+        else:
+            assert (int(s), 512) in covered and (int(s) + n - 512, 512) in covered
+    assert len(runs) == 2 * 3 + 1 + 6
+
+    calls = []
+
+    def fetch(lo, k):
+        calls.append(k)
+        return g[lo:lo + k]
+
+    scan_s, upd_s, n_upd, d, sumsq = bench.oracle_windowed_step(w, fetch, runs, threads=3,
+                                                                piece=100_000)
+    assert max(calls) <= 100_000 and sum(calls[:14]) == w.numel
+    cfg, st = bench._oracle_config(w)
+    inv, inv32 = O.unscale_factor(cfg, st)
+    want, of = O.scan(cfg.dtype, g, inv, inv32)
+    assert of == 0 and abs(sumsq - want) <= 1e-12 * want
+    assert d.skip == 0 and n_upd == sum(k for _, k, _ in runs)
+    assert scan_s > 0 and upd_s > 0
