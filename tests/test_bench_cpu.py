@@ -294,3 +294,17 @@ def test_windowed_cpu_baseline_covers_runs_and_the_whole_norm():
     assert of == 0 and abs(sumsq - want) <= 1e-12 * want
     assert d.skip == 0 and n_upd == sum(k for _, k, _ in runs)
     assert scan_s > 0 and upd_s > 0
+
+
+def test_committed_profiles_were_taken_on_the_current_kernels():
+    """Every rocprofv3 summary under profiles/ records the hash of the kernel sources it
+    was taken on; all of them must match the sources in the tree."""
+    import glob
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt")))
+    assert paths
+    want = bench.kernel_sha()
+    for p in paths:
+        with open(p) as f:
+            shas = [line.split(":", 1)[1].strip() for line in f
+                    if line.startswith("kernel_source_sha256:")]
+        assert shas == [want], (os.path.basename(p), shas)
