@@ -675,6 +675,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
     sl.dtype = cfg->dtype;
     sl.optimizer = cfg->optimizer;
+    sl.norm_nt = plan.numel > kNormCachedMax;
     sl.norm_chunks = h->d_norm_chunks;
     sl.nnorm = nnorm;
     sl.norm_blocks = nb;
@@ -716,7 +717,7 @@ namespace nz1 {
 // norm pass (+ per-segment sums when enabled); snapshots the pre-step state for a fused
 // update
 static hipError_t enqueue_norm(const StepLaunch& s, hipStream_t stream, const KernelTiming& t) {
-    hipError_t e = launch_norm(s.dtype, s.norm_chunks, s.nnorm, s.norm_blocks, s.st, s.partial,
+    hipError_t e = launch_norm(s.dtype, s.norm_nt, s.norm_chunks, s.nnorm, s.norm_blocks, s.st, s.partial,
                                s.fused ? s.snap : nullptr, s.lds.norm, stream, t);
     if (e == hipSuccess && s.seg_sumsq)
         e = launch_segment_sumsq(s.partial, s.seg_range, s.nseg, s.seg_sumsq, stream);

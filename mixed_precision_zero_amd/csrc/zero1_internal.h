@@ -116,6 +116,18 @@ constexpr bool kFuseSmallGrids = NZ1_FUSE_SMALL_GRIDS;
 #endif
 constexpr uint32_t kNormTargetBlocks = NZ1_NORM_TARGET_BLOCKS;
 
+// Shards of at most this many elements read the gradient in the norm pass with
+// cache-allocating loads, so the update's second read of it hits the chip's 256 MB
+// Infinity Cache; larger shards use non-temporal loads (their gradient does not stay
+// resident, and allocating it slows the norm pass: 215M elements 110-117 against 64 us).
+// Measured on MI355X with a 2 GB copy between steps (us per step, non-temporal /
+// cache-allocating): 1M 18.2 / 17.8, 2M 26.7 / 26.1, 4M 38.0 / 36.8, 8M 57.6 / 56.0, 16M
+// 106.6 / 103.0, 24M 144.4 / 142.4, 44M 242 / 245, 215M 1103-1110 / 1137-1140.
+#ifndef NZ1_NORM_CACHED_MAX
+#define NZ1_NORM_CACHED_MAX (1ull << 24)
+#endif
+constexpr uint64_t kNormCachedMax = NZ1_NORM_CACHED_MAX;
+
 // Optional timing of one launch: both null, or two events that receive the kernel's own
 // start and stop time from its dispatch (no marker packets between kernels).
 struct KernelTiming {
@@ -136,9 +148,10 @@ struct FuseIn {
 
 // Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
 // snap (optional): the norm pass copies the pre-step state there for a fused update.
-hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
-                       const DevState* st, double* partial, DevState* snap, uint32_t lds_reserve,
-                       hipStream_t stream, const KernelTiming& t = {});
+// nt_loads: non-temporal gradient loads (else cache-allocating; see kNormCachedMax).
+hipError_t launch_norm(int dtype, bool nt_loads, const Chunk* chunks, uint32_t nchunks,
+                       uint32_t blocks, const DevState* st, double* partial, DevState* snap,
+                       uint32_t lds_reserve, hipStream_t stream, const KernelTiming& t = {});
 // The finalize sums partial[0, nparts) in a fixed order (the norm pass's partials, or the
 // ranks' squared norms of a split step), then takes the step's decisions.
 hipError_t launch_finalize(const double* partial, uint32_t nparts, DevState* st,
@@ -217,6 +230,7 @@ int lds_reserve(int device, int optimizer, uint64_t update_blocks, LdsReserve* o
 // what the allocation-free entry point assembles in its scratch.
 struct StepLaunch {
     int dtype = 0, optimizer = 0;
+    bool norm_nt = true;           // non-temporal gradient loads in the norm pass
     const Chunk* norm_chunks = nullptr;
     uint32_t nnorm = 0, norm_blocks = 0;
     double* partial = nullptr;            // norm_blocks doubles

@@ -85,9 +85,6 @@ struct Fmt<2> {
 // 16-byte global accesses, optionally non-temporal (streamed data is touched once).
 // Compile-time tuning knobs; the defaults are the measured best on MI355X.
 // ------------------------------------------------------------------------------------
-#ifndef NZ1_NORM_NT_LOAD
-#define NZ1_NORM_NT_LOAD 1
-#endif
 #ifndef NZ1_NORM_UNROLL
 #define NZ1_NORM_UNROLL 8
 #endif
@@ -199,8 +196,9 @@ __device__ __forceinline__ void sq8(const uint4 q, float inv, double& a0, double
     }
 }
 
-// This block's sum of squares over its chunks (every thread gets the value).
-template <int DT>
+// This block's sum of squares over its chunks (every thread gets the value).  NTL:
+// non-temporal loads (the gradient is not kept in the caches for the update's re-read).
+template <int DT, bool NTL>
 __device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, uint32_t nchunks,
                                              float inv) {
     double a0 = 0.0, a1 = 0.0;
@@ -217,11 +215,11 @@ __device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, u
             for (; i + (kNormUnroll - 1) * kBlock < nvec; i += kNormUnroll * kBlock) {
                 uint4 q[kNormUnroll];
 #pragma unroll
-                for (int u = 0; u < kNormUnroll; ++u) q[u] = ld16<NZ1_NORM_NT_LOAD>(g4 + i + u * kBlock);
+                for (int u = 0; u < kNormUnroll; ++u) q[u] = ld16<NTL>(g4 + i + u * kBlock);
 #pragma unroll
                 for (int u = 0; u < kNormUnroll; ++u) sq8<DT>(q[u], inv, a0, a1);
             }
-            for (; i < nvec; i += kBlock) sq8<DT>(ld16<NZ1_NORM_NT_LOAD>(g4 + i), inv, a0, a1);
+            for (; i < nvec; i += kBlock) sq8<DT>(ld16<NTL>(g4 + i), inv, a0, a1);
             done = nvec * kVec;
         }
         for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
@@ -234,7 +232,7 @@ __device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, u
 
 // snap (optional): block 0 copies the scaler state the step starts from, for an update
 // that takes the step's decisions itself (see fused_decide).
-template <int DT>
+template <int DT, bool NTL>
 __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ chunks,
                                                       uint32_t nchunks,
                                                       const DevState* __restrict__ st,
@@ -248,7 +246,7 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ 
         snap->step = st->step;
         snap->skipped_total = st->skipped_total;
     }
-    const double s = norm_block<DT>(chunks, nchunks, st->inv);
+    const double s = norm_block<DT, NTL>(chunks, nchunks, st->inv);
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
@@ -905,11 +903,12 @@ static void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t ld
         hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
 }
 
-hipError_t launch_norm(int dtype, const Chunk* chunks, uint32_t nchunks, uint32_t blocks,
-                       const DevState* st, double* partial, DevState* snap, uint32_t lds_reserve,
-                       hipStream_t stream, const KernelTiming& t) {
-    launch(dtype == 1 ? norm_kernel<1> : norm_kernel<2>, dim3(blocks), dim3(kBlock), lds_reserve,
-           stream, t, chunks, nchunks, st, partial, snap);
+hipError_t launch_norm(int dtype, bool nt_loads, const Chunk* chunks, uint32_t nchunks,
+                       uint32_t blocks, const DevState* st, double* partial, DevState* snap,
+                       uint32_t lds_reserve, hipStream_t stream, const KernelTiming& t) {
+    auto k = dtype == 1 ? (nt_loads ? norm_kernel<1, true> : norm_kernel<1, false>)
+                        : (nt_loads ? norm_kernel<2, true> : norm_kernel<2, false>);
+    launch(k, dim3(blocks), dim3(kBlock), lds_reserve, stream, t, chunks, nchunks, st, partial, snap);
     return hipGetLastError();
 }
 
@@ -995,7 +994,7 @@ hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t
 
 hipError_t norm_static_lds(uint32_t* bytes) {
     hipFuncAttributes a{};
-    const hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&norm_kernel<1>));
+    const hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&norm_kernel<1, true>));
     *bytes = e == hipSuccess ? (uint32_t)a.sharedSizeBytes : 0u;
     return e;
 }
