@@ -429,3 +429,35 @@ def test_flat_shard_of_whole_tiles(sizes):
     log(f"case whole tiles {sizes}")
     chk = run_sequence(w, 3, shard=shard, where=f" whole tiles {sizes}")
     assert chk.ost.skipped_total == 1
+
+
+# Shard sizes on either side of the library's size-dependent launch choices: the AdamW
+# update runs 4 blocks per CU up to 16 grid blocks per CU, 8 up to 40, else 2 (on 256 CUs:
+# 4,096 and 10,240 tiles of 2,048 elements), and the norm pass keeps the gradient cached
+# up to 2^24 elements.  Results must not depend on them.
+_BOUNDARY_SIZES = {
+    "grid_16_per_cu": 4096 * 2048,
+    "grid_16_per_cu_plus_one_tile": 4096 * 2048 + 2048,
+    "cached_norm_2e24": 1 << 24,
+    "uncached_norm_2e24_plus_ragged": (1 << 24) + 2048 + 5,
+    "grid_40_per_cu_plus_ragged": 10240 * 2048 + 3,
+}
+
+
+@pytest.mark.parametrize("case", sorted(_BOUNDARY_SIZES))
+def test_launch_choice_boundaries(case):
+    """Every element against the oracle for two steps (the second with clipping active)
+    at each size-dependent launch boundary, on a flat two-segment shard."""
+    n = _BOUNDARY_SIZES[case]
+    w = _custom(f"boundary_{case}", [n - 4099, 4099], [True, False], clip_norm=0.05)
+    shard = DeviceShard(w, flat=True)
+    log(f"case launch boundary {case}: {n} elements")
+    shard.init_()
+    chk = Checker(shard)
+    try:
+        for k in range(2):
+            shard.grads_(k, chk.scale())
+            chk.step(w.hyper.lr, threads=16, where=f" {case} step {k}")
+    finally:
+        chk.close()
+    assert chk.ost.step == 2 and chk.ost.last_coef < 1.0
