@@ -210,12 +210,14 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
  * over every gradient, a one-block finalize (skip decision, clip coefficient, step
  * count, bias corrections, loss-scale update, all on the device), and the fused
  * unscale + clip + AdamW + cast update, which returns before loading its data when the
- * finalize decided to skip.  When the norm pass has at most 256 blocks (shards up to
- * ~8M elements; below ~2M its chunks are shortened so that it still spreads over the
- * chip) there is no separate finalize: every update block sums the partials in the
- * finalize's order and takes the same decisions itself (same bits), and one of them
- * writes the state.  The gradient must be complete in stream order before this
- * call.
+ * finalize decided to skip.  When the norm pass has at most 256 blocks there is no
+ * separate finalize: every update block sums the partials in the finalize's order and
+ * takes the same decisions itself (same bits), and one of them writes the state.  That
+ * is the case for every shard below ~2M elements (a norm pass of at most 64 blocks) and
+ * for every flat partition of fewer than 128 segments whose norm chunks stay within
+ * 2^24 elements (up to ~4e9 elements; a norm pass of at most 256 large blocks);
+ * neox_zero1_plan reports which.  The
+ * gradient must be complete in stream order before this call.
  * On a skipped step master, exp_avg, exp_avg_sq and half are not written.
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
 int neox_zero1_step(neox_zero1* h, float lr, void* hip_stream);
@@ -325,6 +327,10 @@ typedef struct neox_zero1_plan_t {
     uint32_t norm_chunk_elems;     /* norm chunk length                                 */
     uint32_t tile_elems;           /* flat tile length                                  */
     int32_t  update_path;          /* NEOX_PATH_FLAT or NEOX_PATH_CHUNKED               */
+    uint32_t norm_block_threads;   /* threads per block of the norm pass                */
+    uint32_t update_decides;       /* 1: the update takes the step's decisions itself  */
+                                   /*    from the norm pass's partials (no finalize    */
+                                   /*    launch); 0: a one-block finalize decides       */
 } neox_zero1_plan_t;
 
 /* Fills *out (host) and the first min(cap, size) entries of each host table; a table

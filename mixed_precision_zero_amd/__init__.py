@@ -68,7 +68,8 @@ class neox_zero1_plan_t(C.Structure):
     _fields_ = [("numel", C.c_uint64), ("update_chunks", C.c_uint64), ("norm_chunks", C.c_uint64),
                 ("flat_tiles", C.c_uint64), ("flat_changes", C.c_uint64),
                 ("chunk_elems", C.c_uint32), ("norm_chunk_elems", C.c_uint32),
-                ("tile_elems", C.c_uint32), ("update_path", C.c_int32)]
+                ("tile_elems", C.c_uint32), ("update_path", C.c_int32),
+                ("norm_block_threads", C.c_uint32), ("update_decides", C.c_uint32)]
 
 
 class neox_shard_segment(C.Structure):

@@ -431,8 +431,32 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
     // norm pass still spreads over the chip)
     p.C = cfg->chunk_elems ? cfg->chunk_elems : kDefaultChunk;
     for (uint64_t k = 0; k < nseg; ++k) p.numel += segs[k].numel;
+    const bool has_v = cfg->optimizer == NEOX_OPT_ADAMW;
+    uint64_t flat_n = 0;
+    p.flat = !cfg->chunked_update && cfg->chunk_elems == 0 &&
+             flat_layout(segs, nseg, has_v, &flat_n) &&
+             (flat_n + kFlatTile - 1) / kFlatTile * kFlatBlock < (1ull << 32);
     const uint64_t spread = (p.numel + kNormTargetBlocks - 1) / kNormTargetBlocks;
-    const uint64_t target = spread < kNormChunk ? (spread > p.C ? spread : p.C) : kNormChunk;
+    uint64_t target = spread < kNormChunk ? (spread > p.C ? spread : p.C) : kNormChunk;
+    // Above that, a flat partition of fewer than kFuseMaxParts / 2 segments runs its norm
+    // pass as at most kFuseMaxParts large blocks (one per CU, kNormBigBlock threads each),
+    // so that the update takes the step's decisions itself and the finalize launch goes:
+    // chunks of numel / (kFuseMaxParts - nseg) elements, since each segment adds at most
+    // one short chunk.  A shard whose chunks would exceed 2^24 elements keeps the many
+    // short chunks (a few hundred large blocks leave the chip half idle in a last
+    // round).  Measured on MI355X, us per step (short chunks / large blocks): 215M
+    // 1115 / 1101, a Pythia-410M rank 237 / 230, 64M 336 / 327, 16M 84.8 / 82.1, 24M
+    // 123.3 / 124.2; 6e9 (385 large blocks) 31.6 / 31.7 ms.  The chunk-table update
+    // reads its descriptor before its data, so deciding there as well is slower on large
+    // grids (215M 1145 / 1345): other layouts keep the finalize.
+    if (kFuseSmallGrids && p.flat && spread >= kNormChunk && nseg < kFuseMaxParts / 2) {
+        const uint64_t parts = kFuseMaxParts - nseg;
+        const uint64_t few = ((p.numel + parts - 1) / parts + p.C - 1) / p.C * p.C;
+        if (few <= (1u << 24)) {
+            target = few;
+            p.norm_big = true;
+        }
+    }
     const uint64_t C1_64 = (target + p.C - 1) / p.C * p.C;
     p.C1 = C1_64 > (1u << 24) ? p.C : (uint32_t)C1_64;
     try {
@@ -448,11 +472,6 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
                      [](const Chunk& a, const Chunk& b) { return (uintptr_t)a.master < (uintptr_t)b.master; });
 #endif
 
-    const bool has_v = cfg->optimizer == NEOX_OPT_ADAMW;
-    uint64_t flat_n = 0;
-    p.flat = !cfg->chunked_update && cfg->chunk_elems == 0 &&
-             flat_layout(segs, nseg, has_v, &flat_n) &&
-             (flat_n + kFlatTile - 1) / kFlatTile * kFlatBlock < (1ull << 32);
     if (p.flat) {
         try {
             build_flat_tables(segs, nseg, flat_n, p.tile_word, p.change);
@@ -532,10 +551,11 @@ int lds_reserve(int device, int optimizer, uint64_t update_blocks, LdsReserve* o
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
     if (e != hipSuccess) return set_hip_error(e, "hipDeviceGetAttribute");
     if (cus < 1) cus = 1;
-    uint32_t norm_fixed = 0;
-    e = norm_static_lds(&norm_fixed);
+    uint32_t norm_fixed = 0, norm_big_fixed = 0;
+    e = norm_static_lds(&norm_fixed, &norm_big_fixed);
     if (e != hipSuccess) return set_hip_error(e, "hipFuncGetAttributes");
     out->norm = reserve_for(lds_per_cu, NZ1_NORM_BLOCKS_PER_CU, norm_fixed);
+    out->norm_big = reserve_for(lds_per_cu, 1, norm_big_fixed);   // one large block per CU
     // the update kernels declare no static LDS
     if (optimizer == NEOX_OPT_SGD) {
         // momentum SGD keeps its fixed shapes: 8 per CU measured slower at every size
@@ -571,6 +591,10 @@ extern "C" int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment*
     out->norm_chunk_elems = p.C1;
     out->tile_elems = kFlatTile;
     out->update_path = p.flat ? NEOX_PATH_FLAT : NEOX_PATH_CHUNKED;
+    out->norm_block_threads = p.norm_big ? kNormBigBlock : kBlock;
+    uint64_t nb = cfg->norm_blocks ? cfg->norm_blocks : p.norm_table.size();
+    if (nb > p.norm_table.size()) nb = p.norm_table.size();
+    out->update_decides = kFuseSmallGrids && nb <= kFuseMaxParts ? 1 : 0;
     for (uint64_t i = 0; i < chunk_cap && i < p.table.size(); ++i) {
         const Chunk& c = p.table[i];
         const neox_segment& sg = segs[c.seg];
@@ -676,6 +700,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     sl.dtype = cfg->dtype;
     sl.optimizer = cfg->optimizer;
     sl.norm_nt = plan.numel > kNormCachedMax;
+    sl.norm_big = plan.norm_big;
     sl.norm_chunks = h->d_norm_chunks;
     sl.nnorm = nnorm;
     sl.norm_blocks = nb;
@@ -717,8 +742,9 @@ namespace nz1 {
 // norm pass (+ per-segment sums when enabled); snapshots the pre-step state for a fused
 // update
 static hipError_t enqueue_norm(const StepLaunch& s, hipStream_t stream, const KernelTiming& t) {
-    hipError_t e = launch_norm(s.dtype, s.norm_nt, s.norm_chunks, s.nnorm, s.norm_blocks, s.st, s.partial,
-                               s.fused ? s.snap : nullptr, s.lds.norm, stream, t);
+    hipError_t e = launch_norm(s.dtype, s.norm_nt, s.norm_big, s.norm_chunks, s.nnorm,
+                               s.norm_blocks, s.st, s.partial, s.fused ? s.snap : nullptr,
+                               s.norm_big ? s.lds.norm_big : s.lds.norm, stream, t);
     if (e == hipSuccess && s.seg_sumsq)
         e = launch_segment_sumsq(s.partial, s.seg_range, s.nseg, s.seg_sumsq, stream);
     return e;

@@ -9,6 +9,12 @@
 namespace nz1 {
 
 constexpr int kBlock = 256;   // threads per block of the norm, finalize and telemetry kernels
+// Threads per block of the norm pass when it runs as at most kFuseMaxParts large blocks
+// (one per CU) so that the update can take the step's decisions itself; see make_plan.
+#ifndef NZ1_NORM_BIG_BLOCK
+#define NZ1_NORM_BIG_BLOCK 1024
+#endif
+constexpr int kNormBigBlock = NZ1_NORM_BIG_BLOCK;
 constexpr int kVec = 8;       // elements per thread-vector: one 16-byte load of halves
 
 enum : uint32_t {
@@ -149,7 +155,8 @@ struct FuseIn {
 // Launchers (zero1_kernels.hip).  Each returns the hipError_t of its launch.
 // snap (optional): the norm pass copies the pre-step state there for a fused update.
 // nt_loads: non-temporal gradient loads (else cache-allocating; see kNormCachedMax).
-hipError_t launch_norm(int dtype, bool nt_loads, const Chunk* chunks, uint32_t nchunks,
+// big: kNormBigBlock threads per block (else kBlock).
+hipError_t launch_norm(int dtype, bool nt_loads, bool big, const Chunk* chunks, uint32_t nchunks,
                        uint32_t blocks, const DevState* st, double* partial, DevState* snap,
                        uint32_t lds_reserve, hipStream_t stream, const KernelTiming& t = {});
 // The finalize sums partial[0, nparts) in a fixed order (the norm pass's partials, or the
@@ -173,7 +180,8 @@ hipError_t launch_flat_update(int dtype, int optimizer, const FlatSpan& f, const
 
 // Static LDS (bytes) of the norm kernel: launch reservations subtract it so that the
 // requested number of blocks per CU really fits.
-hipError_t norm_static_lds(uint32_t* bytes);
+// Static LDS of the norm kernel at kBlock and at kNormBigBlock threads per block.
+hipError_t norm_static_lds(uint32_t* bytes, uint32_t* big_bytes);
 
 // The unscale factor for scale s, computed in double and rounded once to FP32; the
 // host (initial state) and the finalize kernel evaluate the same expression.
@@ -203,6 +211,7 @@ struct Plan {
     uint32_t C1 = 0;                       // norm chunk length
     std::vector<Chunk> table, norm_table;  // update and norm work tables
     bool flat = false;                     // flat partition: the update runs over tiles
+    bool norm_big = false;                 // the norm pass runs kNormBigBlock-thread blocks
     uint64_t numel = 0;
     std::vector<uint32_t> tile_word, change;
 };
@@ -220,7 +229,7 @@ DevState initial_state(const neox_zero1_config& cfg, float scale, int32_t good_s
 
 // Dynamic LDS each pass's blocks reserve (only to cap blocks per CU) on one device.
 struct LdsReserve {
-    uint32_t norm = 0, update = 0, flat = 0;
+    uint32_t norm = 0, norm_big = 0, update = 0, flat = 0;
 };
 // update_blocks: the update grid (flat tiles or chunk-table entries), which sets how many
 // update blocks share a CU.
@@ -231,6 +240,7 @@ int lds_reserve(int device, int optimizer, uint64_t update_blocks, LdsReserve* o
 struct StepLaunch {
     int dtype = 0, optimizer = 0;
     bool norm_nt = true;           // non-temporal gradient loads in the norm pass
+    bool norm_big = false;         // kNormBigBlock-thread norm blocks
     const Chunk* norm_chunks = nullptr;
     uint32_t nnorm = 0, norm_blocks = 0;
     double* partial = nullptr;            // norm_blocks doubles

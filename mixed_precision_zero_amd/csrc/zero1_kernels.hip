@@ -196,9 +196,10 @@ __device__ __forceinline__ void sq8(const uint4 q, float inv, double& a0, double
     }
 }
 
-// This block's sum of squares over its chunks (every thread gets the value).  NTL:
+// This block's sum of squares over its chunks (every thread gets the value); NB threads
+// per block.  NTL:
 // non-temporal loads (the gradient is not kept in the caches for the update's re-read).
-template <int DT, bool NTL>
+template <int DT, bool NTL, int NB>
 __device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, uint32_t nchunks,
                                              float inv) {
     double a0 = 0.0, a1 = 0.0;
@@ -212,28 +213,28 @@ __device__ __forceinline__ double norm_block(const Chunk* __restrict__ chunks, u
             const uint32_t nvec = len / kVec;
             uint32_t i = threadIdx.x;
             // kNormUnroll loads in flight per thread, then their sums in order
-            for (; i + (kNormUnroll - 1) * kBlock < nvec; i += kNormUnroll * kBlock) {
+            for (; i + (kNormUnroll - 1) * NB < nvec; i += kNormUnroll * NB) {
                 uint4 q[kNormUnroll];
 #pragma unroll
-                for (int u = 0; u < kNormUnroll; ++u) q[u] = ld16<NTL>(g4 + i + u * kBlock);
+                for (int u = 0; u < kNormUnroll; ++u) q[u] = ld16<NTL>(g4 + i + u * NB);
 #pragma unroll
                 for (int u = 0; u < kNormUnroll; ++u) sq8<DT>(q[u], inv, a0, a1);
             }
-            for (; i < nvec; i += kBlock) sq8<DT>(ld16<NTL>(g4 + i), inv, a0, a1);
+            for (; i < nvec; i += NB) sq8<DT>(ld16<NTL>(g4 + i), inv, a0, a1);
             done = nvec * kVec;
         }
-        for (uint32_t i = done + threadIdx.x; i < len; i += kBlock) {
+        for (uint32_t i = done + threadIdx.x; i < len; i += NB) {
             const double x = (double)(Fmt<DT>::one(g[i]) * inv);
             a0 = __builtin_fma(x, x, a0);
         }
     }
-    return block_sum<kBlock>(a0 + a1);
+    return block_sum<NB>(a0 + a1);
 }
 
 // snap (optional): block 0 copies the scaler state the step starts from, for an update
 // that takes the step's decisions itself (see fused_decide).
-template <int DT, bool NTL>
-__global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ chunks,
+template <int DT, bool NTL, int NB>
+__global__ __launch_bounds__(NB) void norm_kernel(const Chunk* __restrict__ chunks,
                                                       uint32_t nchunks,
                                                       const DevState* __restrict__ st,
                                                       double* __restrict__ partial,
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(const Chunk* __restrict__ 
         snap->step = st->step;
         snap->skipped_total = st->skipped_total;
     }
-    const double s = norm_block<DT, NTL>(chunks, nchunks, st->inv);
+    const double s = norm_block<DT, NTL, NB>(chunks, nchunks, st->inv);
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
@@ -903,12 +904,20 @@ static void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t ld
         hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
 }
 
-hipError_t launch_norm(int dtype, bool nt_loads, const Chunk* chunks, uint32_t nchunks,
+hipError_t launch_norm(int dtype, bool nt_loads, bool big, const Chunk* chunks, uint32_t nchunks,
                        uint32_t blocks, const DevState* st, double* partial, DevState* snap,
                        uint32_t lds_reserve, hipStream_t stream, const KernelTiming& t) {
-    auto k = dtype == 1 ? (nt_loads ? norm_kernel<1, true> : norm_kernel<1, false>)
-                        : (nt_loads ? norm_kernel<2, true> : norm_kernel<2, false>);
-    launch(k, dim3(blocks), dim3(kBlock), lds_reserve, stream, t, chunks, nchunks, st, partial, snap);
+    if (big) {
+        auto k = dtype == 1 ? (nt_loads ? norm_kernel<1, true, kNormBigBlock> : norm_kernel<1, false, kNormBigBlock>)
+                            : (nt_loads ? norm_kernel<2, true, kNormBigBlock> : norm_kernel<2, false, kNormBigBlock>);
+        launch(k, dim3(blocks), dim3(kNormBigBlock), lds_reserve, stream, t, chunks, nchunks, st,
+               partial, snap);
+    } else {
+        auto k = dtype == 1 ? (nt_loads ? norm_kernel<1, true, kBlock> : norm_kernel<1, false, kBlock>)
+                            : (nt_loads ? norm_kernel<2, true, kBlock> : norm_kernel<2, false, kBlock>);
+        launch(k, dim3(blocks), dim3(kBlock), lds_reserve, stream, t, chunks, nchunks, st, partial,
+               snap);
+    }
     return hipGetLastError();
 }
 
@@ -992,10 +1001,13 @@ hipError_t launch_update(int dtype, int optimizer, const Chunk* chunks, uint32_t
     return hipGetLastError();
 }
 
-hipError_t norm_static_lds(uint32_t* bytes) {
-    hipFuncAttributes a{};
-    const hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&norm_kernel<1, true>));
+hipError_t norm_static_lds(uint32_t* bytes, uint32_t* big_bytes) {
+    hipFuncAttributes a{}, b{};
+    hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&norm_kernel<1, true, kBlock>));
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&b, reinterpret_cast<const void*>(&norm_kernel<1, true, kNormBigBlock>));
     *bytes = e == hipSuccess ? (uint32_t)a.sharedSizeBytes : 0u;
+    *big_bytes = e == hipSuccess ? (uint32_t)b.sharedSizeBytes : 0u;
     return e;
 }
 

@@ -141,6 +141,7 @@ extern "C" int neox_zero1_step_noalloc(const neox_zero1_config* cfg, const neox_
     sl.dtype = cfg->dtype;
     sl.optimizer = cfg->optimizer;
     sl.norm_nt = plan.numel > kNormCachedMax;
+    sl.norm_big = plan.norm_big;
     sl.norm_chunks = reinterpret_cast<const Chunk*>(base + L.norm_table);
     sl.nnorm = nnorm;
     sl.norm_blocks = nb;

@@ -392,12 +392,15 @@ def test_timing_events_record_and_change_nothing():
     count the steps they cover (up to max_steps), report positive durations that fit in
     the wall-clock time of those steps, and a new begin discards an unfinished one."""
     import time
-    # over 256 norm chunks, so the finalize is its own launch
-    w = _custom("timing", [9_000_000, 7, 1_000_001], [True, False, True])
+    # 133 segments: the norm pass keeps 32K-element chunks (over 256 of them), so the
+    # finalize is its own launch
+    sizes = [9_000_000, 7, 1_000_001] + [33] * 130
+    w = _custom("timing", sizes, [i % 2 == 0 for i in range(len(sizes))])
     stream = torch.cuda.current_stream().cuda_stream
     a, b = DeviceShard(w), DeviceShard(w)
     a.init_()
     b.init_()
+    assert Z.neox_zero1_plan(lib_config(w), a.neox_segments(), tables=False)[0].update_decides == 0
     ha = Z.neox_zero1_create(lib_config(w), a.neox_segments(), stream)
     hb = Z.neox_zero1_create(lib_config(w), b.neox_segments(), stream)
     log("case timing events")

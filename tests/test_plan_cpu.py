@@ -204,3 +204,36 @@ def test_plan_errors():
     cfg2 = _cfg(chunked_update=1)
     assert L.neox_zero1_plan(C.byref(cfg2), arr2, 2, C.byref(out), two, 2, None, 0, None, 0) == Z.NEOX_OK
     assert as_tuples(two) == as_tuples(full[:2]) and out.update_chunks == len(full)
+
+
+@pytest.mark.parametrize("sizes", [[3_000_000], [2_000_000, 97, 1_500_000], [70_000_000] * 3,
+                                   [1 << 31, 1 << 31], [9_000] * 200 + [5_000_000]],
+                         ids=["3m", "3_segments", "210m", "4e9", "201_segments"])
+def test_norm_pass_of_few_large_blocks(sizes):
+    """Above 64 norm chunks of 32K elements, a flat partition of fewer than 128 segments
+    gets at most 256 norm chunks of numel / (256 - nseg) elements (a multiple of the
+    update chunk), run as 1,024-thread blocks, and the update takes the decisions itself;
+    with 128 or more segments, chunks beyond 2^24 elements or the chunk-table update, it
+    keeps 32K-element chunks of 256-thread blocks and a finalize."""
+    decays = [i % 3 != 1 for i in range(len(sizes))]
+    segs = flat_segments(sizes, decays)
+    plan = Z.neox_zero1_plan(_cfg(), segs, tables=False)[0]
+    n, nseg, C = sum(sizes), len(sizes), plan.chunk_elems
+    parts = 256 - nseg
+    few = -(-(-(-n // parts)) // C) * C
+    if nseg < 128 and few <= 1 << 24:
+        assert plan.norm_chunk_elems == few and plan.norm_block_threads == 1024
+        assert plan.norm_chunks <= 256 and plan.update_decides == 1
+    else:
+        assert plan.norm_chunk_elems == 32768 and plan.norm_block_threads == 256
+        assert plan.norm_chunks > 256 and plan.update_decides == 0
+    if n < 1 << 31:      # the reference table of a 4e9-element shard is too slow to list
+        assert plan.norm_chunks == len(expected_chunks(segs, plan.norm_chunk_elems))
+    # a requested smaller striding grid decides by itself too
+    plan = Z.neox_zero1_plan(_cfg(norm_blocks=200), segs, tables=False)[0]
+    assert plan.update_decides == 1
+    # the chunk-table update keeps the short norm chunks and the finalize
+    plan = Z.neox_zero1_plan(_cfg(chunked_update=1), segs, tables=False)[0]
+    assert plan.norm_chunk_elems == 32768 and plan.norm_block_threads == 256
+    assert plan.update_path == Z.NEOX_PATH_CHUNKED
+    assert plan.update_decides == (plan.norm_chunks <= 256)

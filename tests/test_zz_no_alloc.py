@@ -108,25 +108,37 @@ def test_noalloc_equals_step_two_calls_second_smaller():
 
 
 
-def test_noalloc_equals_step_with_a_separate_finalize_and_sgd():
-    """A 9M-element flat shard, whose norm pass has more than 256 blocks so the step runs
-    its separate finalize launch (the first test's shards take the decision in the
-    update), checked against the oracle too; then a smaller momentum-SGD shard in
-    separate allocations."""
-    sizes = [6_000_000, 7, 3_000_001]
-    big = W.Workload("noalloc_flat_9m", 73, [(n, k != 1) for k, n in enumerate(sizes)], W.Hyper(),
-                     steps=2)
+def _fake_flat(sizes, decays):
+    """Segments of a flat layout at fake addresses: the plan only compares them."""
     base, off, fake = 1 << 36, 0, []
-    for n in sizes:               # addresses of a flat layout, only compared by the plan
+    for n, d in zip(sizes, decays):
         fake.append(Z.neox_segment(base + 2 * off, base + (1 << 34) + 2 * off,
                                    base + 2 * (1 << 34) + 4 * off, base + 3 * (1 << 34) + 4 * off,
-                                   base + 4 * (1 << 34) + 4 * off, n, 1, 0, 0))
+                                   base + 4 * (1 << 34) + 4 * off, n,
+                                   Z.NEOX_SEG_DECAY if d else 0, 0, 0))
         off += n
-    plan, _, _, _ = Z.neox_zero1_plan(lib_config(big), fake, tables=False)
-    assert plan.norm_chunks > 256, plan.norm_chunks
-    log(f"case noalloc flat 9M: {big.numel} elements, {plan.norm_chunks} norm chunks")
-    st = _run_pair(big, 2, flat=True, misalign=(0, 0, 0, 0, 0), oracle_check=True)
-    assert (st.step, st.skipped_total) == (2, 0)
+    return fake
+
+
+def test_noalloc_equals_step_on_large_norm_blocks_a_separate_finalize_and_sgd():
+    """A 9M-element flat shard of three segments, whose norm pass runs as at most 256
+    large blocks and whose update takes the decisions itself; the same with 130 more
+    small segments, which keeps the norm pass's short chunks (over 256) and the separate
+    finalize launch; both checked against the oracle too.  Then a smaller momentum-SGD
+    shard in separate allocations."""
+    for name, wid, sizes, decides in (("noalloc_flat_9m_large_blocks", 73,
+                                       [6_000_000, 7, 3_000_001], 1),
+                                      ("noalloc_flat_9m_finalize", 75,
+                                       [6_000_000, 7, 3_000_001] + [41] * 130, 0)):
+        decays = [k % 2 == 0 for k in range(len(sizes))]
+        big = W.Workload(name, wid, list(zip(sizes, decays)), W.Hyper(), steps=2)
+        plan, _, _, _ = Z.neox_zero1_plan(lib_config(big), _fake_flat(sizes, decays),
+                                          tables=False)
+        assert plan.update_decides == decides, (name, plan.norm_chunks)
+        log(f"case {name}: {big.numel} elements, {plan.norm_chunks} norm chunks of "
+            f"{plan.norm_block_threads} threads")
+        st = _run_pair(big, 2, flat=True, misalign=(0, 0, 0, 0, 0), oracle_check=True)
+        assert (st.step, st.skipped_total) == (2, 0)
 
     sgd = W.Workload("noalloc_sep_sgd", 74, [(30_000, True), (1_001, False)],
                      W.Hyper(optimizer=1), steps=3, injections={1: [(7, "nan")]})
