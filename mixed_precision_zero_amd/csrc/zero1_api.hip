@@ -62,6 +62,11 @@ namespace {
 #ifndef NZ1_NORM_BLOCKS_PER_CU
 #define NZ1_NORM_BLOCKS_PER_CU 4
 #endif
+// Longest norm chunk of the large-block norm pass: 2^28 elements, so that every shard
+// one GPU can hold (~1.8e10 elements at 16 bytes each) fits 256 chunks.
+#ifndef NZ1_NORM_BIG_MAX_CHUNK
+#define NZ1_NORM_BIG_MAX_CHUNK (1u << 28)
+#endif
 #ifndef NZ1_FLAT_BLOCKS_PER_CU
 #define NZ1_FLAT_BLOCKS_PER_CU 2
 #endif
@@ -442,23 +447,24 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
     // pass as at most kFuseMaxParts large blocks (one per CU, kNormBigBlock threads each),
     // so that the update takes the step's decisions itself and the finalize launch goes:
     // chunks of numel / (kFuseMaxParts - nseg) elements, since each segment adds at most
-    // one short chunk.  A shard whose chunks would exceed 2^24 elements keeps the many
-    // short chunks (a few hundred large blocks leave the chip half idle in a last
-    // round).  Measured on MI355X, us per step (short chunks / large blocks): 215M
-    // 1115 / 1101, a Pythia-410M rank 237 / 230, 64M 336 / 327, 16M 84.8 / 82.1, 24M
-    // 123.3 / 124.2; 6e9 (385 large blocks) 31.6 / 31.7 ms.  The chunk-table update
+    // one short chunk (up to NZ1_NORM_BIG_MAX_CHUNK elements; a longer shard keeps the
+    // many short chunks).  Measured on MI355X, us per step (short chunks / large blocks):
+    // 215M 1115 / 1101, a Pythia-410M rank 237 / 230, 64M 336 / 327, 16M 84.8 / 82.1,
+    // 24M 123.3 / 124.2; 6e9 31.53 / 31.15 ms (215 chunks of 27.9M elements; capped at
+    // 2^24 elements the 385 large blocks leave the chip half idle in a last round:
+    // 31.7 ms).  The chunk-table update
     // reads its descriptor before its data, so deciding there as well is slower on large
     // grids (215M 1145 / 1345): other layouts keep the finalize.
     if (kFuseSmallGrids && p.flat && spread >= kNormChunk && nseg < kFuseMaxParts / 2) {
         const uint64_t parts = kFuseMaxParts - nseg;
         const uint64_t few = ((p.numel + parts - 1) / parts + p.C - 1) / p.C * p.C;
-        if (few <= (1u << 24)) {
+        if (few <= (uint64_t)NZ1_NORM_BIG_MAX_CHUNK) {
             target = few;
             p.norm_big = true;
         }
     }
     const uint64_t C1_64 = (target + p.C - 1) / p.C * p.C;
-    p.C1 = C1_64 > (1u << 24) ? p.C : (uint32_t)C1_64;
+    p.C1 = C1_64 > (p.norm_big ? (uint64_t)NZ1_NORM_BIG_MAX_CHUNK : (1u << 24)) ? p.C : (uint32_t)C1_64;
     try {
         build_chunks(segs, nseg, p.C, p.table);
         build_chunks(segs, nseg, p.C1, p.norm_table);

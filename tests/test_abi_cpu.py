@@ -242,4 +242,13 @@ def test_noalloc_validates_before_any_device_work():
     with pytest.raises(Z.NeoxError) as e:
         Z.neox_zero1_step_noalloc(Z.neox_zero1_default_config(chunked_update=1), [big], st, 1e-3)
     assert e.value.code == Z.NEOX_EINVAL and "scratch" in str(e.value)
+    # a flat partition needs ~2 bytes per 1,000 elements (its tile table): 9e9 is beyond
+    n = 9_000_000_000
+    flat = Z.neox_segment(1 << 44, 1 << 45, 1 << 46, (1 << 46) + (1 << 45), 1 << 47, n,
+                          Z.NEOX_SEG_DECAY, 0, 0)
+    plan = Z.neox_zero1_plan(Z.neox_zero1_default_config(), [flat], tables=False)[0]
+    assert plan.update_path == Z.NEOX_PATH_FLAT and plan.update_decides == 1
+    with pytest.raises(Z.NeoxError) as e:
+        Z.neox_zero1_step_noalloc(Z.neox_zero1_default_config(), [flat], st, 1e-3)
+    assert e.value.code == Z.NEOX_EINVAL and "scratch" in str(e.value)
     assert Z.NEOX_NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024

@@ -213,7 +213,7 @@ def test_norm_pass_of_few_large_blocks(sizes):
     """Above 64 norm chunks of 32K elements, a flat partition of fewer than 128 segments
     gets at most 256 norm chunks of numel / (256 - nseg) elements (a multiple of the
     update chunk), run as 1,024-thread blocks, and the update takes the decisions itself;
-    with 128 or more segments, chunks beyond 2^24 elements or the chunk-table update, it
+    with 128 or more segments, chunks beyond 2^28 elements or the chunk-table update, it
     keeps 32K-element chunks of 256-thread blocks and a finalize."""
     decays = [i % 3 != 1 for i in range(len(sizes))]
     segs = flat_segments(sizes, decays)
@@ -221,7 +221,7 @@ def test_norm_pass_of_few_large_blocks(sizes):
     n, nseg, C = sum(sizes), len(sizes), plan.chunk_elems
     parts = 256 - nseg
     few = -(-(-(-n // parts)) // C) * C
-    if nseg < 128 and few <= 1 << 24:
+    if nseg < 128 and few <= 1 << 28:
         assert plan.norm_chunk_elems == few and plan.norm_block_threads == 1024
         assert plan.norm_chunks <= 256 and plan.update_decides == 1
     else:
