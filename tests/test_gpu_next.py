@@ -188,7 +188,8 @@ def test_split_step_ranks_match_the_global_oracle(D):
                     assert_close("exp_avg", post["m"], o["m"], sm, tag)
                     assert_close("exp_avg_sq", post["v"], o["v"], sv, tag)
                     assert_close("master", post["master"], o["master"], sw, tag)
-                    assert_half_close(post["half"], o["half"], tag)
+                    assert_half_close(post["half"], o["half"], tag, rk["shard"].w.hyper.dtype,
+                                      o["master"], sw)
             log(f"  step {k}: skip={d.skip} norm={ost.last_norm:.4g} ranks agree with the oracle")
         assert ost.skipped_total == 1
     finally:

@@ -436,21 +436,27 @@ def test_flat_shard_of_whole_tiles(sizes):
 # 4,096 and 10,240 tiles of 2,048 elements), and the norm pass keeps the gradient cached
 # up to 2^24 elements.  Results must not depend on them.
 _BOUNDARY_SIZES = {
-    "grid_16_per_cu": 4096 * 2048,
-    "grid_16_per_cu_plus_one_tile": 4096 * 2048 + 2048,
-    "cached_norm_2e24": 1 << 24,
-    "uncached_norm_2e24_plus_ragged": (1 << 24) + 2048 + 5,
-    "grid_40_per_cu_plus_ragged": 10240 * 2048 + 3,
+    "grid_16_per_cu": (4096 * 2048, W.F16),
+    "grid_16_per_cu_plus_one_tile": (4096 * 2048 + 2048, W.F16),
+    "cached_norm_2e24": (1 << 24, W.F16),
+    "uncached_norm_2e24_plus_ragged": ((1 << 24) + 2048 + 5, W.F16),
+    "grid_40_per_cu_plus_ragged": (10240 * 2048 + 3, W.F16),
+    "large_norm_blocks_bf16": (3_000_007, W.BF16),
+    "short_norm_chunks_2e6": (64 * 32767, W.F16),
 }
 
 
 @pytest.mark.parametrize("case", sorted(_BOUNDARY_SIZES))
 def test_launch_choice_boundaries(case):
     """Every element against the oracle for two steps (the second with clipping active)
-    at each size-dependent launch boundary, on a flat two-segment shard."""
-    n = _BOUNDARY_SIZES[case]
-    w = _custom(f"boundary_{case}", [n - 4099, 4099], [True, False], clip_norm=0.05)
+    at each size-dependent launch boundary, on a flat two-segment shard; the norm pass
+    runs as large blocks above 64 chunks of 32K elements and the update decides."""
+    n, dtype = _BOUNDARY_SIZES[case]
+    w = _custom(f"boundary_{case}", [n - 4099, 4099], [True, False], dtype=dtype, clip_norm=0.05)
     shard = DeviceShard(w, flat=True)
+    plan = Z.neox_zero1_plan(lib_config(w), shard.neox_segments(), tables=False)[0]
+    assert plan.update_decides == 1
+    assert plan.norm_block_threads == (1024 if -(-n // 64) >= 32768 else 256), plan.norm_block_threads
     log(f"case launch boundary {case}: {n} elements")
     shard.init_()
     chk = Checker(shard)
