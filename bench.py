@@ -762,6 +762,14 @@ def alloc_shard(w, dev, sgd):
     return keep, segs
 
 
+def norm_plan(Z, cfg, segs):
+    """How the norm pass runs and who decides, from the library's own plan."""
+    plan = Z.neox_zero1_plan(cfg, segs, tables=False)[0]
+    return {"norm_blocks": min(plan.norm_chunks, cfg.norm_blocks or plan.norm_chunks),
+            "norm_block_threads": plan.norm_block_threads,
+            "update_decides": bool(plan.update_decides)}
+
+
 def lib_config(Z, w, **over):
     return Z.neox_zero1_default_config(
         beta1=w.hyper.beta1, beta2=w.hyper.beta2, eps=w.hyper.eps,
@@ -822,9 +830,11 @@ def extra_workload(name, dev, steps, warmup):
           flush=True)
     keep, segs = alloc_shard(w, dev, sgd=False)
     stream = torch.cuda.current_stream()
-    h = Z.neox_zero1_create(lib_config(Z, w), segs, stream.cuda_stream)
+    cfg = lib_config(Z, w)
+    h = Z.neox_zero1_create(cfg, segs, stream.cuda_stream)
     try:
         flat_path = Z.neox_zero1_update_path(h) == Z.NEOX_PATH_FLAT
+        plan_info = norm_plan(Z, cfg, segs)
 
         def one_step():
             Z.neox_zero1_step(h, w.hyper.lr, stream.cuda_stream)
@@ -844,7 +854,7 @@ def extra_workload(name, dev, steps, warmup):
     return {"params": n, "segments": len(w.segments),
             "layout": "flat shard" if w.flat else "separate allocations",
             "grad_dtype": "f16" if w.hyper.dtype == W.F16 else "bf16",
-            "update_path": "flat" if flat_path else "chunked",
+            "update_path": "flat" if flat_path else "chunked", **plan_info,
             "steps": steps, "warmup": warmup,
             "value": n / (t["wall_ms"] * 1e-3), "unit": "params/s",
             "ms_per_step": t["wall_ms"], "ms_per_step_median": t["step_median_ms"],
@@ -950,10 +960,11 @@ def main():
 
     keep, segs = alloc_shard(w, dev, sgd)
     stream = torch.cuda.current_stream()
-    h = Z.neox_zero1_create(lib_config(Z, w, segment_norms=int(args.segment_norms),
-                                       chunked_update=int(args.chunked_update)),
-                            segs, stream.cuda_stream)
+    cfg = lib_config(Z, w, segment_norms=int(args.segment_norms),
+                     chunked_update=int(args.chunked_update))
+    h = Z.neox_zero1_create(cfg, segs, stream.cuda_stream)
     flat_path = Z.neox_zero1_update_path(h) == Z.NEOX_PATH_FLAT
+    plan_info = norm_plan(Z, cfg, segs)
     loc = torch.zeros(1, dtype=torch.float64, device=dev)
 
     def one_step():
@@ -1021,7 +1032,7 @@ def main():
                    "layout": "flat shard" if w.flat else "separate allocations",
                    "optimizer": args.optimizer, "split": args.split,
                    "segment_norms": args.segment_norms, "graph": args.graph,
-                   "update_path": "flat" if flat_path else "chunked"},
+                   "update_path": "flat" if flat_path else "chunked", **plan_info},
         "hbm": {"step_bytes": step_bpp * n,
                 "step_gbps": step_bpp * n / (ms_per_step * 1e-3) / 1e9,
                 "step_frac_of_peak": step_bpp * n / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
