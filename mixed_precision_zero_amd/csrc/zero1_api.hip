@@ -455,7 +455,7 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
     // 31.7 ms).  The chunk-table update
     // reads its descriptor before its data, so deciding there as well is slower on large
     // grids (215M 1145 / 1345): other layouts keep the finalize.
-    if (kFuseSmallGrids && p.flat && spread >= kNormChunk && nseg < kFuseMaxParts / 2) {
+    if (kUpdateDecides && p.flat && spread >= kNormChunk && nseg < kFuseMaxParts / 2) {
         const uint64_t parts = kFuseMaxParts - nseg;
         const uint64_t few = ((p.numel + parts - 1) / parts + p.C - 1) / p.C * p.C;
         if (few <= (uint64_t)NZ1_NORM_BIG_MAX_CHUNK) {
@@ -600,7 +600,7 @@ extern "C" int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment*
     out->norm_block_threads = p.norm_big ? kNormBigBlock : kBlock;
     uint64_t nb = cfg->norm_blocks ? cfg->norm_blocks : p.norm_table.size();
     if (nb > p.norm_table.size()) nb = p.norm_table.size();
-    out->update_decides = kFuseSmallGrids && nb <= kFuseMaxParts ? 1 : 0;
+    out->update_decides = kUpdateDecides && nb <= kFuseMaxParts ? 1 : 0;
     for (uint64_t i = 0; i < chunk_cap && i < p.table.size(); ++i) {
         const Chunk& c = p.table[i];
         const neox_segment& sg = segs[c.seg];
@@ -713,7 +713,7 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
     sl.partial = h->d_partial;
     sl.st = h->d_state;
     sl.snap = h->d_state + 1;
-    sl.fused = kFuseSmallGrids && nb <= kFuseMaxParts;
+    sl.fused = kUpdateDecides && nb <= kFuseMaxParts;
     sl.fin = finalize_args(*cfg);
     sl.upd = update_args(*cfg);
     sl.flat = flat;

@@ -107,12 +107,14 @@ struct UpdateArgs {
 };
 
 // A norm pass of at most this many blocks hands its partials straight to the update,
-// which then takes the step's decisions itself (no finalize launch).
+// which then takes the step's decisions itself (no finalize launch): every shard below
+// ~2M elements, and flat partitions of fewer than kFuseMaxParts / 2 segments, whose
+// norm pass then runs as large blocks (see make_plan).  0 = always a separate finalize.
 constexpr uint32_t kFuseMaxParts = 256;
-#ifndef NZ1_FUSE_SMALL_GRIDS
-#define NZ1_FUSE_SMALL_GRIDS 1
+#ifndef NZ1_UPDATE_DECIDES
+#define NZ1_UPDATE_DECIDES 1
 #endif
-constexpr bool kFuseSmallGrids = NZ1_FUSE_SMALL_GRIDS;
+constexpr bool kUpdateDecides = NZ1_UPDATE_DECIDES;
 // Small shards split the norm pass into at least about this many blocks (shorter norm
 // chunks, down to the update chunk length).  On the 1M-element shard: 11.4-11.5 us per
 // step at 64, 11.9-12.1 at 16, 12.7-12.8 at 256 (whose fused update sums four waves of

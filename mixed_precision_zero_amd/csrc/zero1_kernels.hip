@@ -812,7 +812,8 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
     // Wait for the decision before loading: a skipped step then reads nothing here.  The
     // base pointers are 16-byte aligned, so their low-bit term never fires; it makes the
     // branch wait for them too, so they are fetched with the state pointer, not after.
-    // (With FUSE the decision is not made yet: small shards load speculatively.)
+    // (With FUSE the decision is not made yet: the block issues its tile's loads first and
+    // decides behind them, so a skipped step still reads every tile.)
     if constexpr (!FUSE) {
         const uintptr_t low = ((uintptr_t)s.grad | (uintptr_t)s.half | (uintptr_t)s.master |
                                (uintptr_t)s.m | (uintptr_t)s.v) & 1u;

@@ -148,7 +148,7 @@ extern "C" int neox_zero1_step_noalloc(const neox_zero1_config* cfg, const neox_
     sl.partial = reinterpret_cast<double*>(base + L.partial);
     sl.st = d_state;
     sl.snap = d_state + 1;
-    sl.fused = kFuseSmallGrids && nb <= kFuseMaxParts;
+    sl.fused = kUpdateDecides && nb <= kFuseMaxParts;
     sl.fin = finalize_args(*cfg);
     sl.upd = update_args(*cfg);
     sl.lds = lds;
