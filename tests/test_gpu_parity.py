@@ -150,6 +150,30 @@ def test_overflow_from_unscale_factor():
         chk.close()
 
 
+def test_overflow_decided_on_the_fp32_product():
+    """x = (1 + 2^-7) 2^126 in bf16 times a pre-divide factor whose FP32 rounding pushes
+    the product past the FP32 range (the exact product stays below it): the step skips,
+    as the oracle decides in FP32; without that element the step is clean."""
+    x, inv = (1 + 2.0 ** -7) * 2.0 ** 126, 3.9689921219219535
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(x) * np.float32(inv)) and np.isfinite(np.float32(x * inv))
+    w = _custom("fp32_window", [1000], [True], W.BF16, predivide_factor=inv)
+    shard = DeviceShard(w)
+    shard.init_()
+    chk = Checker(shard)
+    try:
+        W.device_grads_(w, shard.segs[0]["grad"], 0, 1.0)
+        shard.segs[0]["grad"][517] = x
+        assert float(shard.segs[0]["grad"][517]) == x
+        gst, d = chk.step(1e-3, where=" fp32 window")
+        assert d.skip == 1 and gst.skipped_total == 1
+        W.device_grads_(w, shard.segs[0]["grad"], 1, 1.0)
+        gst, d = chk.step(1e-3, where=" clean")
+        assert d.skip == 0
+    finally:
+        chk.close()
+
+
 def test_resume_equals_continuous():
     """N steps, destroy, re-create with the state read back, M steps == N+M steps."""
     w = _custom("resume", [30_000, 2048], [True, False], growth_interval=2)

@@ -91,3 +91,13 @@ def test_rounding_exhaustive_all_fp32(cast_check, dtype):
         res = list(ex.map(run, ranges))
     bad = [(r, first) for r, (n, first) in zip(ranges, res) if n]
     assert not bad, f"mismatches, first input bits {hex(bad[0][1])}"
+
+
+def test_nan_becomes_the_quiet_nan_with_its_sign():
+    """A NaN casts to the quiet NaN of the half format (all-ones exponent, top mantissa
+    bit set), keeping the sign; infinities stay infinities."""
+    for dtype, qnan, inf in ((O.F16, 0x7E00, 0x7C00), (O.BF16, 0x7FC0, 0x7F80)):
+        x = np.array([np.nan, -np.nan, np.inf, -np.inf], np.float32)
+        x[1] = -np.abs(x[1])
+        got = O.float_to_half(dtype, x)
+        assert [int(v) for v in got] == [qnan, qnan | 0x8000, inf, inf | 0x8000], (dtype, got)

@@ -66,6 +66,40 @@ MUTANTS = [
      "double m1 = mu * m0 + g;", "double m1 = mu * m0 + (1.0 - mu) * g;", 1),
     ("shard length not padded to D x align",
      "uint64_t padded = (total + unit - 1) / unit * unit;", "uint64_t padded = total;", 1),
+    ("SGD decay dropped", "if (decay) u += wd * w0;", "if (0) u += wd * w0;", 2),
+    ("SGD update sign flipped", "double w1 = w0 - rate * u;", "double w1 = w0 + rate * u;", 2),
+    ("bf16 exponent bias off by one",
+     "f.exp_bits = 8; f.bias = 127;", "f.exp_bits = 8; f.bias = 126;", 1),
+    ("NaN encoded without the quiet bit",
+     "(uint16_t)(1u << (f.mant_bits - 1));", "(uint16_t)1u;", 1),
+    ("largest finite rounds to infinity",
+     "if (r > max_finite) return sign | all_ones_exp;",
+     "if (r >= max_finite) return sign | all_ones_exp;", 1),
+    ("partition tensor offset from the rank start",
+     "s->tensor_offset = e - tstart;", "s->tensor_offset = e - (uint64_t)rank * P;", 1),
+    ("growth by the back-off factor",
+     "scale_times(st->loss_scale, cfg->growth_factor)",
+     "scale_times(st->loss_scale, cfg->backoff_factor)", 1),
+    ("overflow run not reset by a clean step", "    st->consecutive_overflows = 0;\n", "", 1),
+    ("skipped step reports norm 0", "st->last_norm = INFINITY;", "st->last_norm = 0.0;", 1),
+    ("decay applied to no-decay elements", "if (decay) u += wd * w0;", "u += wd * w0;", 1),
+    ("clip below the threshold",
+     "norm > cfg->clip_norm) coef", "norm >= cfg->clip_norm * 0.5) coef", 1),
+    ("m and v from the unclipped gradient",
+     "double g = (x * d->inv) * d->coef;", "double g = (x * d->inv);", 1),
+    ("second moment not bias-corrected",
+     "double den = sqrt(v1 / d->bc2) + eps;", "double den = sqrt(v1) + eps;", 1),
+    ("static scaler backs off",
+     "if (cfg->scaler_mode == ORC_DYNAMIC) {\n            float s = scale_times",
+     "if (1) {\n            float s = scale_times", 1),
+    ("partition padding to D only",
+     "uint64_t unit = (uint64_t)dp_world_size * (uint64_t)align;",
+     "uint64_t unit = (uint64_t)dp_world_size;", 1),
+    ("half copy cast from the unrounded master",
+     "half[i] = orc_float_to_half(cfg->dtype, wf);",
+     "half[i] = orc_float_to_half(cfg->dtype, (float)(w1 * (1 + 1e-7)));", 1),
+    ("overflow taken on the double product",
+     "float g32 = (float)x * inv32;", "float g32 = (float)(x * inv);", 1),
 ]
 
 PINS = [os.path.join(ROOT, "tests", f) for f in

@@ -154,6 +154,19 @@ def test_eps_zero_is_undefined_at_a_zero_gradient():
     assert np.isfinite(s["master"][[1, 3]]).all()
 
 
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_half_copy_is_the_cast_of_the_stored_master(dtype):
+    """The half copy is the FP32 master as stored, rounded to the half format."""
+    n = 5000
+    rng = np.random.default_rng(21)
+    cfg = O.Config(dtype=dtype, scaler_mode=O.STATIC)
+    st = O.Scaler(loss_scale=1.0)
+    s = make_state(n, 22, dtype)
+    for k in range(3):
+        run_step(cfg, st, np.float32(3e-3), grads_from(rng.standard_normal(n) * 1e-2, dtype), s)
+        assert np.array_equal(s["half"], O.float_to_half(dtype, s["master"]))
+
+
 def test_decay_only_and_identity():
     """g = 0: moments stay 0 and the update is pure decoupled decay, w*(1-lr*wd);
     a no-decay segment is left bitwise unchanged."""
@@ -231,6 +244,14 @@ def test_clip_norm_after_clip():
 
 
 def test_clip_inactive_below_threshold_and_disabled():
+    # clipping only above the threshold: a norm of exactly c (four gradients of 0.5,
+    # exact in fp16) and of 0.8c keep the coefficient at 1; 1.25c gives 0.8
+    for vals, c, want in (([0.5] * 4, 1.0, 1.0), ([0.4] * 4, 1.0, 1.0), ([0.625] * 4, 1.0, 0.8)):
+        st = O.Scaler(loss_scale=1.0)
+        g = grads_from(vals)
+        s = make_state(4, 16)
+        run_step(O.Config(clip_norm=c), st, np.float32(1e-3), g, s)
+        assert abs(st.last_coef - want) <= 1e-15, (vals, st.last_coef)
     n = 1000
     grad = grads_from(np.full(n, 0.01))
     for c in (1.0, 0.0, -1.0):
@@ -296,6 +317,32 @@ def test_overflow_from_unscale_in_fp32():
     assert st.last_skipped == 0
 
 
+# x * inv overflows FP32 when both are rounded to FP32 first, but not when the product
+# is taken in double and rounded once: x = (1 + 2^-7) 2^126 (exact in bf16), inv a double
+# just below the threshold whose FP32 rounding lies above it.
+OVERFLOW_WINDOW_X = (1 + 2.0 ** -7) * 2.0 ** 126
+OVERFLOW_WINDOW_INV = 3.9689921219219535
+
+
+def test_overflow_is_decided_on_the_fp32_product():
+    """Reading: the unscaled gradient is the FP32 value fp32(x) * fp32(inv); a value that
+    overflows there is an overflow even where the exact product would round to a finite
+    FP32 number."""
+    x, inv = OVERFLOW_WINDOW_X, OVERFLOW_WINDOW_INV
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(x) * np.float32(inv)) and np.isfinite(np.float32(x * inv))
+    g = O.float_to_half(O.BF16, np.array([x, 1.0], np.float32))
+    assert O.half_to_double(O.BF16, g)[0] == x
+    cfg = O.Config(dtype=O.BF16, scaler_mode=O.STATIC, predivide_factor=inv)
+    st = O.Scaler(loss_scale=1.0)
+    i, i32 = O.unscale_factor(cfg, st)
+    assert i == inv and i32 == np.float32(inv)
+    _, of = O.scan(O.BF16, g, i, i32)
+    assert of == 1
+    _, of = O.scan(O.BF16, g[1:], i, i32)
+    assert of == 0
+
+
 def _scaler_model(seq, S0, interval, min_scale, growth=2.0, backoff=0.5):
     """Run-length model: split the sequence at overflows; within a clean run the scale
     doubles once per full `interval` clean steps counted from the run's start (or from
@@ -336,11 +383,13 @@ def test_scaler_every_sequence_of_length_12():
 
 
 def test_static_scaler_never_moves():
-    cfg = O.Config(scaler_mode=O.STATIC, growth_interval=1)
-    st = O.Scaler(loss_scale=1.0)
-    for o in (0, 1, 1, 0, 0, 0, 1):
-        O.decide(cfg, st, o, 0.0)
-    assert st.loss_scale == 1.0 and st.skipped_total == 3 and st.step == 4
+    # also above the floor, where a back-off would show
+    for S in (1.0, 1024.0):
+        cfg = O.Config(scaler_mode=O.STATIC, growth_interval=1)
+        st = O.Scaler(loss_scale=S)
+        for o in (0, 1, 1, 0, 0, 0, 1):
+            O.decide(cfg, st, o, 0.0)
+        assert st.loss_scale == S and st.skipped_total == 3 and st.step == 4
 
 
 def test_scale_floor_and_collapse_counter():
