@@ -275,7 +275,19 @@ static void push_chunk(std::vector<Chunk>& t, const neox_segment& s, uint32_t se
     t.push_back(c);
 }
 
+// Entries build_chunks makes for chunk length C.
+static uint64_t count_chunks(const neox_segment* segs, uint64_t nseg, uint32_t C) {
+    uint64_t n = 0;
+    for (uint64_t s = 0; s < nseg; ++s) {
+        const int head = vector_head(segs[s]);
+        const uint64_t h = head > 0 ? ((uint64_t)head < segs[s].numel ? (uint64_t)head : segs[s].numel) : 0;
+        n += (h ? 1 : 0) + (segs[s].numel - h + C - 1) / C;
+    }
+    return n;
+}
+
 static void build_chunks(const neox_segment* segs, uint64_t nseg, uint32_t C, std::vector<Chunk>& t) {
+    t.reserve(count_chunks(segs, nseg, C));
     for (uint64_t s = 0; s < nseg; ++s) {
         const neox_segment& sg = segs[s];
         const int head = vector_head(sg);
@@ -422,7 +434,8 @@ static void free_handle(neox_zero1* h) {
 
 namespace nz1 {
 
-int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg, Plan& p) {
+int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg, Plan& p,
+              bool want_table) {
     if (!cfg) return set_error(NEOX_EINVAL, "cfg is NULL");
     int rc = validate_config(cfg);
     if (rc) return rc;
@@ -465,14 +478,16 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
     }
     const uint64_t C1_64 = (target + p.C - 1) / p.C * p.C;
     p.C1 = C1_64 > (p.norm_big ? (uint64_t)NZ1_NORM_BIG_MAX_CHUNK : (1u << 24)) ? p.C : (uint32_t)C1_64;
+    p.nchunks = count_chunks(segs, nseg, p.C);
+    // one block per chunk of the chunked update; the grid's x size in work-items is 32-bit
+    if (!p.flat && p.nchunks >= (1ull << 24))
+        return set_error(NEOX_EINVAL, "%llu chunks: raise chunk_elems", (unsigned long long)p.nchunks);
     try {
-        build_chunks(segs, nseg, p.C, p.table);
+        if (!p.flat || want_table) build_chunks(segs, nseg, p.C, p.table);
         build_chunks(segs, nseg, p.C1, p.norm_table);
     } catch (const std::exception&) {
         return set_error(NEOX_ENOMEM, "host allocation of the chunk table");
     }
-    // one block per chunk; the grid's x size in work-items is 32-bit
-    if (p.table.size() >= (1ull << 24)) return set_error(NEOX_EINVAL, "%zu chunks: raise chunk_elems", p.table.size());
 #if NZ1_SORT_CHUNKS
     std::stable_sort(p.table.begin(), p.table.end(),
                      [](const Chunk& a, const Chunk& b) { return (uintptr_t)a.master < (uintptr_t)b.master; });
@@ -585,11 +600,11 @@ extern "C" int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment*
     if ((chunk_cap && !chunks) || (word_cap && !tile_words) || (change_cap && !changes))
         return set_error(NEOX_EINVAL, "NULL table with a nonzero capacity");
     Plan p;
-    const int rc = make_plan(cfg, segs, nseg, p);
+    const int rc = make_plan(cfg, segs, nseg, p, chunk_cap > 0);
     if (rc) return rc;
     std::memset(out, 0, sizeof *out);
     out->numel = p.numel;
-    out->update_chunks = p.table.size();
+    out->update_chunks = p.nchunks;
     out->norm_chunks = p.norm_table.size();
     out->flat_tiles = p.flat ? p.tile_word.size() - 1 : 0;
     out->flat_changes = p.change.size();
@@ -601,7 +616,7 @@ extern "C" int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment*
     uint64_t nb = cfg->norm_blocks ? cfg->norm_blocks : p.norm_table.size();
     if (nb > p.norm_table.size()) nb = p.norm_table.size();
     out->update_decides = kUpdateDecides && nb <= kFuseMaxParts ? 1 : 0;
-    for (uint64_t i = 0; i < chunk_cap && i < p.table.size(); ++i) {
+    for (uint64_t i = 0; i < chunk_cap && i < p.table.size(); ++i) {   // built when chunk_cap > 0
         const Chunk& c = p.table[i];
         const neox_segment& sg = segs[c.seg];
         chunks[i].offset = (uint64_t)(c.master - sg.master);

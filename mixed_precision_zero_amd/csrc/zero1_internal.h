@@ -212,14 +212,17 @@ struct Plan {
     uint32_t C = 0;                        // update chunk length
     uint32_t C1 = 0;                       // norm chunk length
     std::vector<Chunk> table, norm_table;  // update and norm work tables
+    uint64_t nchunks = 0;                  // update chunks (table.size() when it is built)
     bool flat = false;                     // flat partition: the update runs over tiles
     bool norm_big = false;                 // the norm pass runs kNormBigBlock-thread blocks
     uint64_t numel = 0;
     std::vector<uint32_t> tile_word, change;
 };
-// Validates the config and the segments, then builds the tables.  NEOX_OK or an error
-// code (the message recorded).
-int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg, Plan& p);
+// Validates the config and the segments, then builds the tables.  The update chunk table
+// of a flat partition, which the flat update does not read, is built only when
+// `want_table` asks for it.  NEOX_OK or an error code (the message recorded).
+int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t nseg, Plan& p,
+              bool want_table = false);
 
 // Launch constants derived from a validated config.
 FinalizeArgs finalize_args(const neox_zero1_config& cfg);

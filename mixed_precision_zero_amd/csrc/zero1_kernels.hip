@@ -1,6 +1,6 @@
 // zero1_kernels.hip -- gfx950 kernels of the ZeRO-1 mixed-precision Adam step.
 //
-// Three launches per step, all on the caller's stream:
+// Two or three launches per step, all on the caller's stream:
 //   norm      one block per chunk (or a smaller grid striding over the chunks);
 //             each block sums the squares of its unscaled FP32 gradient in double and
 //             writes one partial.  A non-finite unscaled value makes its square, and so
@@ -9,11 +9,13 @@
 //             overflowed".
 //   finalize  one block; fixed-order sum of the per-block partials, then the skip
 //             decision, clip coefficient, step count, bias corrections and the loss
-//             scale update, written to the device state block.
-//   update    returns at once on a skipped step, otherwise unscale + clip + AdamW +
-//             cast with 16-byte loads and stores: flat_update_kernel (one block per
-//             2,048-element tile of a flat partition, addresses from the block index)
-//             or update_kernel (one block per entry of the chunk table, any layout).
+//             scale update, written to the device state block.  Not launched when the
+//             norm pass has at most kFuseMaxParts blocks: then every update block sums
+//             the partials in the finalize's order and decides itself (fused_decide).
+//   update    unscale + clip + AdamW + cast with 16-byte loads and stores, nothing
+//             written on a skipped step: flat_update_kernel (one block per 2,048-element
+//             tile of a flat partition, addresses from the block index) or update_kernel
+//             (one block per entry of the chunk table, any layout).
 // Sources: FP32 Adam state with FP16 weights and dynamic loss scaling [OPT: Open
 // Pre-trained Transformer Language Models, paper card, 计算设置]; pre-divide factor
 // and clipping at 1.0 / 0.3 [same card, 方法适配]; each rank updates only its shard
