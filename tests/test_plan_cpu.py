@@ -206,6 +206,22 @@ def test_plan_errors():
     assert as_tuples(two) == as_tuples(full[:2]) and out.update_chunks == len(full)
 
 
+def test_flat_partition_beyond_the_chunk_table_limit():
+    """The flat update reads no chunk table, so a flat shard of 2^35 elements (2^24 update
+    chunks, more than the chunked update's grid takes) still plans as flat: 2^24 tiles,
+    at most 255 norm chunks, the update deciding.  Forced onto the chunk table, the same
+    shard is refused."""
+    n, S = 1 << 35, 1 << 40
+    segs = [Z.neox_segment(BASE, BASE + S, BASE + 2 * S, BASE + 3 * S, BASE + 4 * S, n,
+                           Z.NEOX_SEG_DECAY, 0, 0)]
+    plan = Z.neox_zero1_plan(_cfg(), segs, tables=False)[0]
+    assert plan.update_path == Z.NEOX_PATH_FLAT and plan.flat_tiles == 1 << 24
+    assert plan.update_chunks == 1 << 24 and plan.norm_chunks <= 255 and plan.update_decides == 1
+    with pytest.raises(Z.NeoxError) as e:
+        Z.neox_zero1_plan(_cfg(chunked_update=1), segs, tables=False)
+    assert e.value.code == Z.NEOX_EINVAL and "chunks" in str(e.value)
+
+
 @pytest.mark.parametrize("sizes", [[3_000_000], [2_000_000, 97, 1_500_000], [70_000_000] * 3,
                                    [1 << 31, 1 << 31], [9_000] * 200 + [5_000_000]],
                          ids=["3m", "3_segments", "210m", "4e9", "201_segments"])
