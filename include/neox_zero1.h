@@ -213,10 +213,11 @@ int neox_zero1_create(const neox_zero1_config* cfg, const neox_segment* segs, ui
  * finalize decided to skip.  When the norm pass has at most 256 blocks there is no
  * separate finalize: every update block sums the partials in the finalize's order and
  * takes the same decisions itself (same bits), and one of them writes the state.  That
- * is the case for every shard below ~2M elements (a norm pass of at most 64 blocks) and
- * for every flat partition of fewer than 128 segments whose norm chunks stay within
- * 2^28 elements (up to ~6.8e10 elements; a norm pass of at most 256 large blocks);
- * neox_zero1_plan reports which.  The
+ * is the case for every flat partition up to ~6.8e10 elements (a norm pass of at most
+ * 64 blocks below ~2M elements, else of at most 256 large blocks cutting the whole
+ * gradient; with segment_norms the chunks follow the segments, which keeps this for
+ * fewer than 128 segments) and for other layouts below ~2M elements whose segments add
+ * few norm chunks; neox_zero1_plan reports which.  The
  * gradient must be complete in stream order before this call.
  * On a skipped step master, exp_avg, exp_avg_sq and half are not written.
  * Errors: NEOX_EINVAL (null handle, non-finite lr), NEOX_EHIP (launch failure). */
@@ -354,9 +355,9 @@ int neox_zero1_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint
  * before it returns.
  * The library's side of the step (state block, per-block partial sums, work tables) lives
  * in a fixed device array of NEOX_NOALLOC_SCRATCH_BYTES that each device holds for the
- * life of the process: about 2 bytes per 1,000 elements on a flat partition of fewer
- * than 128 segments (up to ~8.5e9 elements), 4.2 per 1,000 on other flat partitions (up
- * to ~4e9) and 33 per 1,000 on other layouts (up to ~5e8).  A larger shard is
+ * life of the process: about 2 bytes per 1,000 elements on a flat partition (its tile
+ * table; up to ~8.5e9 elements) and 33 per 1,000 on other layouts (up to ~5e8).  A
+ * larger shard is
  * rejected with NEOX_EINVAL.  Every call on one device uses the same array: calls on one
  * device from several host threads are serialized by the library; calls from several
  * processes each have their own array.

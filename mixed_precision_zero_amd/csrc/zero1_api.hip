@@ -456,20 +456,25 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
              (flat_n + kFlatTile - 1) / kFlatTile * kFlatBlock < (1ull << 32);
     const uint64_t spread = (p.numel + kNormTargetBlocks - 1) / kNormTargetBlocks;
     uint64_t target = spread < kNormChunk ? (spread > p.C ? spread : p.C) : kNormChunk;
-    // Above that, a flat partition of fewer than kFuseMaxParts / 2 segments runs its norm
-    // pass as at most kFuseMaxParts large blocks (one per CU, kNormBigBlock threads each),
-    // so that the update takes the step's decisions itself and the finalize launch goes:
-    // chunks of numel / (kFuseMaxParts - nseg) elements, since each segment adds at most
-    // one short chunk (up to NZ1_NORM_BIG_MAX_CHUNK elements; a longer shard keeps the
-    // many short chunks).  Measured on MI355X, us per step (short chunks / large blocks):
-    // 215M 1115 / 1101, a Pythia-410M rank 237 / 230, 64M 336 / 327, 16M 84.8 / 82.1,
-    // 24M 123.3 / 124.2; 6e9 31.53 / 31.15 ms (215 chunks of 27.9M elements; capped at
-    // 2^24 elements the 385 large blocks leave the chip half idle in a last round:
-    // 31.7 ms).  The chunk-table update
-    // reads its descriptor before its data, so deciding there as well is slower on large
-    // grids (215M 1145 / 1345): other layouts keep the finalize.
-    if (kUpdateDecides && p.flat && spread >= kNormChunk && nseg < kFuseMaxParts / 2) {
-        const uint64_t parts = kFuseMaxParts - nseg;
+    // Above that, a flat partition runs its norm pass as at most kFuseMaxParts large
+    // blocks (one per CU, kNormBigBlock threads each), so that the update takes the step's
+    // decisions itself and the finalize launch goes.  Its gradient is one contiguous array,
+    // so the chunks cut it into kFuseMaxParts equal pieces whatever its segments -- unless
+    // per-segment norms are asked for: then the chunks follow the segments, numel /
+    // (kFuseMaxParts - nseg) elements each (each segment adds at most one short chunk), for
+    // fewer than kFuseMaxParts / 2 segments.  A chunk holds at most NZ1_NORM_BIG_MAX_CHUNK
+    // elements; a longer shard keeps the many short chunks.  Measured on MI355X, us per
+    // step (short chunks and a finalize / large blocks): 215M 1115 / 1101, a Pythia-410M
+    // rank 237 / 230, 64M 336 / 327, 16M 84.8 / 82.1, 24M 123.3 / 124.2; 6e9 31.53 / 31.15
+    // ms (capped at 2^24 elements the 385 large blocks leave the chip half idle in a last
+    // round: 31.7 ms); the 5,000-tensor list carved into one flat partition 5.41 / 5.36 ms.
+    // Chunks across segments instead of along them: 6e9 norm pass 1.81 -> 1.77 ms, 215M
+    // and a Pythia rank unchanged.  The chunk-table update reads its descriptor before its
+    // data, so deciding there as well is slower on large grids (215M 1145 / 1345): other
+    // layouts keep the finalize.
+    const bool span = p.flat && !cfg->segment_norms;
+    if (kUpdateDecides && p.flat && spread >= kNormChunk && (span || nseg < kFuseMaxParts / 2)) {
+        const uint64_t parts = span ? kFuseMaxParts : kFuseMaxParts - nseg;
         const uint64_t few = ((p.numel + parts - 1) / parts + p.C - 1) / p.C * p.C;
         if (few <= (uint64_t)NZ1_NORM_BIG_MAX_CHUNK) {
             target = few;
@@ -484,7 +489,14 @@ int make_plan(const neox_zero1_config* cfg, const neox_segment* segs, uint64_t n
         return set_error(NEOX_EINVAL, "%llu chunks: raise chunk_elems", (unsigned long long)p.nchunks);
     try {
         if (!p.flat || want_table) build_chunks(segs, nseg, p.C, p.table);
-        build_chunks(segs, nseg, p.C1, p.norm_table);
+        if (span) {
+            // the whole gradient as one segment (the norm pass reads only the gradient)
+            neox_segment whole = segs[0];
+            whole.numel = flat_n;
+            build_chunks(&whole, 1, p.C1, p.norm_table);
+        } else {
+            build_chunks(segs, nseg, p.C1, p.norm_table);
+        }
     } catch (const std::exception&) {
         return set_error(NEOX_ENOMEM, "host allocation of the chunk table");
     }

@@ -107,9 +107,10 @@ struct UpdateArgs {
 };
 
 // A norm pass of at most this many blocks hands its partials straight to the update,
-// which then takes the step's decisions itself (no finalize launch): every shard below
-// ~2M elements, and flat partitions of fewer than kFuseMaxParts / 2 segments, whose
-// norm pass then runs as large blocks (see make_plan).  0 = always a separate finalize.
+// which then takes the step's decisions itself (no finalize launch): flat partitions,
+// whose norm pass runs as at most this many large blocks when the shard is not small,
+// and other layouts below ~2M elements whose segments add few norm chunks (see
+// make_plan).  0 = always a separate finalize.
 constexpr uint32_t kFuseMaxParts = 256;
 #ifndef NZ1_UPDATE_DECIDES
 #define NZ1_UPDATE_DECIDES 1

@@ -30,10 +30,11 @@ def _outputs(shard):
 @pytest.mark.parametrize("sizes", [[70_001, 4096, 33], [3000] * 150, [1000] * 256],
                          ids=["38_parts", "150_parts", "256_parts"])
 def test_split_step_equals_step_on_one_rank(sizes):
-    """step == step_local followed by step_apply on the local value, bit for bit.  These
-    shards' norm passes have at most 256 blocks, so the step's update takes the decisions
-    itself while the split step's finalize takes them: the two must agree bit for bit,
-    whether the partials fill one wave of the finalize or all four."""
+    """step == step_local followed by step_apply on the local value, bit for bit.  With
+    per-segment norms the norm chunks follow the segments, so these shards' norm passes
+    have from 38 up to 256 blocks; the step's update takes the decisions itself while the
+    split step's finalize takes them: the two must agree bit for bit, whether the
+    partials fill one wave of the finalize or all four."""
     w = _custom("split1", sizes, [k % 3 != 1 for k in range(len(sizes))], clip_norm=0.05)
     w.injections = {2: [(10, "nan")]}
     stream = torch.cuda.current_stream().cuda_stream
@@ -41,9 +42,11 @@ def test_split_step_equals_step_on_one_rank(sizes):
     for mode in ("step", "split"):
         sh = DeviceShard(w)
         sh.init_()
-        h = Z.neox_zero1_create(lib_config(w), sh.neox_segments(), stream)
-        plan, _, _, _ = Z.neox_zero1_plan(lib_config(w), sh.neox_segments(), tables=False)
-        assert plan.norm_chunks <= 256, plan.norm_chunks
+        cfg = lib_config(w, segment_norms=1)
+        h = Z.neox_zero1_create(cfg, sh.neox_segments(), stream)
+        plan, _, _, _ = Z.neox_zero1_plan(cfg, sh.neox_segments(), tables=False)
+        assert plan.norm_chunks <= 256 and plan.update_decides == 1, plan.norm_chunks
+        assert plan.norm_chunks >= min(38, len(sizes)), plan.norm_chunks
         loc = torch.zeros(1, dtype=torch.float64, device="cuda")
         st_seq = []
         for k in range(5):
@@ -393,12 +396,12 @@ def test_timing_events_record_and_change_nothing():
     count the steps they cover (up to max_steps), report positive durations that fit in
     the wall-clock time of those steps, and a new begin discards an unfinished one."""
     import time
-    # 133 segments: the norm pass keeps 32K-element chunks (over 256 of them), so the
-    # finalize is its own launch
+    # separate allocations: the norm pass keeps 32K-element chunks (over 256 of them), so
+    # the finalize is its own launch
     sizes = [9_000_000, 7, 1_000_001] + [33] * 130
     w = _custom("timing", sizes, [i % 2 == 0 for i in range(len(sizes))])
     stream = torch.cuda.current_stream().cuda_stream
-    a, b = DeviceShard(w), DeviceShard(w)
+    a, b = DeviceShard(w, flat=False), DeviceShard(w, flat=False)
     a.init_()
     b.init_()
     assert Z.neox_zero1_plan(lib_config(w), a.neox_segments(), tables=False)[0].update_decides == 0

@@ -370,7 +370,10 @@ def test_flat_mixed_decay_tiles(dtype):
 @pytest.mark.parametrize("optimizer", [0, 1], ids=["adamw", "sgd"])
 def test_flat_equals_chunked_bitwise(optimizer):
     """Both update kernels run the same arithmetic, so on the same inputs they agree bit
-    for bit: master, m, v, half and the scaler state, over clean and skipped steps."""
+    for bit: master, m, v, half and the scaler state, over clean and skipped steps.  (With
+    per-segment norms, so that both norm passes cut the same chunks: a flat partition's
+    norm chunks otherwise run across segment bounds, which changes the squared norm's
+    summation order.)"""
     w = _custom("flat_vs_chunked", _MIXED_SIZES * 3, _MIXED_DECAY * 3, optimizer=optimizer,
                 weight_decay=0.5)
     w.injections = {1: [(70_000, "+inf")], 3: [(w.numel - 1, "-inf")]}
@@ -379,7 +382,8 @@ def test_flat_equals_chunked_bitwise(optimizer):
     for chunked in (0, 1):
         shard = DeviceShard(w, flat=True)
         shard.init_()
-        h = Z.neox_zero1_create(lib_config(w, chunked_update=chunked, optimizer=optimizer),
+        h = Z.neox_zero1_create(lib_config(w, chunked_update=chunked, optimizer=optimizer,
+                                           segment_norms=1),
                                 shard.neox_segments(), stream)
         assert Z.neox_zero1_update_path(h) == (Z.NEOX_PATH_CHUNKED if chunked else Z.NEOX_PATH_FLAT)
         log(f"case flat vs chunked optimizer={optimizer} chunked={chunked}")

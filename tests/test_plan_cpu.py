@@ -67,6 +67,13 @@ def expected_chunks(segs, C):
     return out
 
 
+def whole_span(segs):
+    """One segment covering a flat partition's arrays from its first segment's start."""
+    s = segs[0]
+    return Z.neox_segment(s.grad, s.half, s.master, s.exp_avg, s.exp_avg_sq,
+                          sum(x.numel for x in segs), s.flags, 0, 0)
+
+
 def as_tuples(chunks):
     return [(c.offset, c.seg, c.len, c.flags) for c in chunks]
 
@@ -137,7 +144,9 @@ def test_chunk_table_bruteforce(chunk):
         C1 = plan.norm_chunk_elems
         target = min(32768, max(C, -(-sum(sizes) // 64)))
         assert C1 % C == 0 and C1 >= target and C1 - C < target
-        assert plan.norm_chunks == len(expected_chunks(segs, C1))
+        # a flat partition's norm chunks cut the whole gradient, across segment bounds
+        norm_segs = [whole_span(segs)] if plan.update_path == Z.NEOX_PATH_FLAT else segs
+        assert plan.norm_chunks == len(expected_chunks(norm_segs, C1))
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -216,7 +225,7 @@ def test_flat_partition_beyond_the_chunk_table_limit():
                            Z.NEOX_SEG_DECAY, 0, 0)]
     plan = Z.neox_zero1_plan(_cfg(), segs, tables=False)[0]
     assert plan.update_path == Z.NEOX_PATH_FLAT and plan.flat_tiles == 1 << 24
-    assert plan.update_chunks == 1 << 24 and plan.norm_chunks <= 255 and plan.update_decides == 1
+    assert plan.update_chunks == 1 << 24 and plan.norm_chunks <= 256 and plan.update_decides == 1
     with pytest.raises(Z.NeoxError) as e:
         Z.neox_zero1_plan(_cfg(chunked_update=1), segs, tables=False)
     assert e.value.code == Z.NEOX_EINVAL and "chunks" in str(e.value)
@@ -226,17 +235,23 @@ def test_flat_partition_beyond_the_chunk_table_limit():
                                    [1 << 31, 1 << 31], [9_000] * 200 + [5_000_000]],
                          ids=["3m", "3_segments", "210m", "4e9", "201_segments"])
 def test_norm_pass_of_few_large_blocks(sizes):
-    """Above 64 norm chunks of 32K elements, a flat partition of fewer than 128 segments
-    gets at most 256 norm chunks of numel / (256 - nseg) elements (a multiple of the
-    update chunk), run as 1,024-thread blocks, and the update takes the decisions itself;
-    with 128 or more segments, chunks beyond 2^28 elements or the chunk-table update, it
-    keeps 32K-element chunks of 256-thread blocks and a finalize."""
+    """Above 64 norm chunks of 32K elements, a flat partition's norm pass cuts its whole
+    gradient into at most 256 chunks of numel / 256 elements (a multiple of the update
+    chunk), whatever its segments, run as 1,024-thread blocks, and the update takes the
+    decisions itself.  With per-segment norms the chunks must follow the segments: fewer
+    than 128 segments give chunks of numel / (256 - nseg) elements, more keep 32K-element
+    chunks of 256-thread blocks and a finalize; so does the chunk-table update."""
     decays = [i % 3 != 1 for i in range(len(sizes))]
     segs = flat_segments(sizes, decays)
+    n, nseg = sum(sizes), len(sizes)
     plan = Z.neox_zero1_plan(_cfg(), segs, tables=False)[0]
-    n, nseg, C = sum(sizes), len(sizes), plan.chunk_elems
-    parts = 256 - nseg
-    few = -(-(-(-n // parts)) // C) * C
+    C = plan.chunk_elems
+    few = -(-(-(-n // 256)) // C) * C
+    assert plan.norm_chunk_elems == few and plan.norm_block_threads == 1024
+    assert plan.norm_chunks == -(-n // few) <= 256 and plan.update_decides == 1
+    # per-segment norms
+    plan = Z.neox_zero1_plan(_cfg(segment_norms=1), segs, tables=False)[0]
+    few = -(-(-(-n // (256 - nseg))) // C) * C
     if nseg < 128 and few <= 1 << 28:
         assert plan.norm_chunk_elems == few and plan.norm_block_threads == 1024
         assert plan.norm_chunks <= 256 and plan.update_decides == 1
@@ -245,8 +260,8 @@ def test_norm_pass_of_few_large_blocks(sizes):
         assert plan.norm_chunks > 256 and plan.update_decides == 0
     if n < 1 << 31:      # the reference table of a 4e9-element shard is too slow to list
         assert plan.norm_chunks == len(expected_chunks(segs, plan.norm_chunk_elems))
-    # a requested smaller striding grid decides by itself too
-    plan = Z.neox_zero1_plan(_cfg(norm_blocks=200), segs, tables=False)[0]
+    # a requested striding grid of at most 256 blocks decides on any layout
+    plan = Z.neox_zero1_plan(_cfg(chunked_update=1, norm_blocks=200), segs, tables=False)[0]
     assert plan.update_decides == 1
     # the chunk-table update keeps the short norm chunks and the finalize
     plan = Z.neox_zero1_plan(_cfg(chunked_update=1), segs, tables=False)[0]

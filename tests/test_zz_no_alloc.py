@@ -120,24 +120,35 @@ def _fake_flat(sizes, decays):
     return fake
 
 
+def _fake_separate(sizes, decays):
+    """Segments in separate fake allocations (16-byte aligned): the plan only compares them."""
+    fake = []
+    for i, (n, d) in enumerate(zip(sizes, decays)):
+        base = (1 << 40) + i * (1 << 38)
+        fake.append(Z.neox_segment(base, base + (1 << 34), base + 2 * (1 << 34),
+                                   base + 3 * (1 << 34), base + 4 * (1 << 34), n,
+                                   Z.NEOX_SEG_DECAY if d else 0, i, 0))
+    return fake
+
+
 def test_noalloc_equals_step_on_large_norm_blocks_a_separate_finalize_and_sgd():
-    """A 9M-element flat shard of three segments, whose norm pass runs as at most 256
-    large blocks and whose update takes the decisions itself; the same with 130 more
-    small segments, which keeps the norm pass's short chunks (over 256) and the separate
-    finalize launch; both checked against the oracle too.  Then a smaller momentum-SGD
-    shard in separate allocations."""
-    for name, wid, sizes, decides in (("noalloc_flat_9m_large_blocks", 73,
-                                       [6_000_000, 7, 3_000_001], 1),
-                                      ("noalloc_flat_9m_finalize", 75,
-                                       [6_000_000, 7, 3_000_001] + [41] * 130, 0)):
-        decays = [k % 2 == 0 for k in range(len(sizes))]
+    """A 9M-element flat shard of 133 segments, whose norm pass runs as at most 256 large
+    blocks across the segments and whose update takes the decisions itself; the same
+    segments in separate allocations, which keep the norm pass's short chunks (over 256)
+    and the separate finalize launch; both checked against the oracle too.  Then a smaller
+    momentum-SGD shard in separate allocations."""
+    sizes = [6_000_000, 7, 3_000_001] + [41] * 130
+    decays = [k % 2 == 0 for k in range(len(sizes))]
+    for name, wid, flat, decides in (("noalloc_flat_9m_large_blocks", 73, True, 1),
+                                     ("noalloc_separate_9m_finalize", 75, False, 0)):
         big = W.Workload(name, wid, list(zip(sizes, decays)), W.Hyper(), steps=2)
-        plan, _, _, _ = Z.neox_zero1_plan(lib_config(big), _fake_flat(sizes, decays),
-                                          tables=False)
+        fake = _fake_flat(sizes, decays) if flat else _fake_separate(sizes, decays)
+        plan, _, _, _ = Z.neox_zero1_plan(lib_config(big), fake, tables=False)
         assert plan.update_decides == decides, (name, plan.norm_chunks)
+        assert plan.update_path == (Z.NEOX_PATH_FLAT if flat else Z.NEOX_PATH_CHUNKED)
         log(f"case {name}: {big.numel} elements, {plan.norm_chunks} norm chunks of "
             f"{plan.norm_block_threads} threads")
-        st = _run_pair(big, 2, flat=True, misalign=(0, 0, 0, 0, 0), oracle_check=True)
+        st = _run_pair(big, 2, flat=flat, misalign=(0, 0, 0, 0, 0), oracle_check=True)
         assert (st.step, st.skipped_total) == (2, 0)
 
     sgd = W.Workload("noalloc_sep_sgd", 74, [(30_000, True), (1_001, False)],
