@@ -459,6 +459,30 @@ def test_flat_shard_of_whole_tiles(sizes):
     assert chk.ost.skipped_total == 1
 
 
+def test_norm_chunks_across_many_segments():
+    """A flat partition of 600 segments (~2.7M elements, bf16, clipping active): its norm
+    pass cuts the gradient into at most 256 large chunks across segment bounds and the
+    update decides.  Every element against the oracle over three steps, the second with
+    a NaN; then the same shard with per-segment norms, whose 600+ chunks follow the
+    segments and keep the finalize launch."""
+    rng = np.random.default_rng(61)
+    sizes = [int(x) for x in rng.integers(1, 9000, 600)]
+    decays = [bool(x) for x in rng.integers(0, 2, 600)]
+    w = _custom("many_segments", sizes, decays, W.BF16, clip_norm=0.05)
+    w.injections = {1: [(int(rng.integers(0, w.numel)), "nan")]}
+    for seg_norms, decides in ((0, 1), (1, 0)):
+        shard = DeviceShard(w, flat=True)
+        plan = Z.neox_zero1_plan(lib_config(w, segment_norms=seg_norms), shard.neox_segments(),
+                                 tables=False)[0]
+        assert plan.update_path == Z.NEOX_PATH_FLAT and plan.update_decides == decides
+        assert (plan.norm_chunks <= 256) == bool(decides) and (plan.norm_block_threads == 1024) == bool(decides)
+        log(f"case many segments segment_norms={seg_norms}: {w.numel} elements, "
+            f"{plan.norm_chunks} norm chunks")
+        chk = run_sequence(w, 3, shard=shard, where=f" many segments {seg_norms}",
+                           segment_norms=seg_norms)
+        assert chk.ost.skipped_total == 1 and chk.ost.last_coef < 1.0
+
+
 # Shard sizes on either side of the library's size-dependent launch choices: the AdamW
 # update runs 4 blocks per CU up to 16 grid blocks per CU, 8 up to 40, else 2 (on 256 CUs:
 # 4,096 and 10,240 tiles of 2,048 elements), and the norm pass keeps the gradient cached
