@@ -126,6 +126,11 @@ constexpr int kUpdateBlock = NZ1_UPDATE_BLOCK;   // threads per block of the chu
 #ifndef NZ1_UPDATE_FAST_DIV
 #define NZ1_UPDATE_FAST_DIV 0
 #endif
+// Pause of a deciding AdamW flat-update block after its loads, in units of 64 clocks
+// (s_sleep); 0 = none.  See flat_update_kernel.
+#ifndef NZ1_FLAT_PAUSE
+#define NZ1_FLAT_PAUSE 8
+#endif
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -836,6 +841,14 @@ __global__ __launch_bounds__(kFlatBlock) void flat_update_kernel(FlatSpan s,
         // Then the decision, the coefficients and the tile words, as vector loads issued
         // behind the data (see ld_after), or the block's own decision (FUSE).
         if constexpr (FUSE) after_data(fin_in);
+        // A deciding AdamW block pauses briefly after issuing its tile's loads, before it
+        // takes the decision and computes.  Measured on MI355X (215M-element shard, same
+        // process, alternating builds, us per update): no pause 1026-1031, 6 x 64 clocks
+        // 1013-1016, 8 x 64 1005-1009, 12 x 64 1013-1017, 16 x 64 1024-1027, 24 x 64
+        // 1055-1057; a Pythia-410M rank, 16M and 1M shards and momentum SGD unchanged.
+        // (Extra ALU work in the same place gives the same gain at the same length: the
+        // gain is the timing, not the work.)
+        if constexpr (FUSE && OPT == 0 && NZ1_FLAT_PAUSE > 0) __builtin_amdgcn_s_sleep(NZ1_FLAT_PAUSE);
         const StepWords sw = step_words<FUSE>(st, tile_word + T, f, fin_in);
         const Coefs c{sw.gscale, sw.rbc1, sw.rsbc2};
         const uint32_t first = sw.w0 >> 1, end = sw.w1 >> 1;
