@@ -11,8 +11,12 @@ namespace nz1 {
 constexpr int kBlock = 256;   // threads per block of the norm, finalize and telemetry kernels
 // Threads per block of the norm pass when it runs as at most kFuseMaxParts large blocks
 // (one per CU) so that the update can take the step's decisions itself; see make_plan.
+// Measured on MI355X (215M-element shard, same process, us per norm pass): 256 threads
+// 103, 512 65.6-66.2, 768 65.7-67.0, 1,024 67.4-67.9; 512 with 12 or 16 loads in flight
+// per thread 64.9-65.4 or 122 (a Pythia-410M rank: 512 16.3-17.0, 1,024 16.9-17.9, 512
+// with 12 loads 18.4-19.1).
 #ifndef NZ1_NORM_BIG_BLOCK
-#define NZ1_NORM_BIG_BLOCK 1024
+#define NZ1_NORM_BIG_BLOCK 512
 #endif
 constexpr int kNormBigBlock = NZ1_NORM_BIG_BLOCK;
 constexpr int kVec = 8;       // elements per thread-vector: one 16-byte load of halves

@@ -475,7 +475,7 @@ def test_norm_chunks_across_many_segments():
         plan = Z.neox_zero1_plan(lib_config(w, segment_norms=seg_norms), shard.neox_segments(),
                                  tables=False)[0]
         assert plan.update_path == Z.NEOX_PATH_FLAT and plan.update_decides == decides
-        assert (plan.norm_chunks <= 256) == bool(decides) and (plan.norm_block_threads == 1024) == bool(decides)
+        assert (plan.norm_chunks <= 256) == bool(decides) and (plan.norm_block_threads == 512) == bool(decides)
         log(f"case many segments segment_norms={seg_norms}: {w.numel} elements, "
             f"{plan.norm_chunks} norm chunks")
         chk = run_sequence(w, 3, shard=shard, where=f" many segments {seg_norms}",
@@ -508,7 +508,7 @@ def test_launch_choice_boundaries(case):
     shard = DeviceShard(w, flat=True)
     plan = Z.neox_zero1_plan(lib_config(w), shard.neox_segments(), tables=False)[0]
     assert plan.update_decides == 1
-    assert plan.norm_block_threads == (1024 if -(-n // 64) >= 32768 else 256), plan.norm_block_threads
+    assert plan.norm_block_threads == (512 if -(-n // 64) >= 32768 else 256), plan.norm_block_threads
     log(f"case launch boundary {case}: {n} elements")
     shard.init_()
     chk = Checker(shard)

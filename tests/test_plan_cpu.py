@@ -237,7 +237,7 @@ def test_flat_partition_beyond_the_chunk_table_limit():
 def test_norm_pass_of_few_large_blocks(sizes):
     """Above 64 norm chunks of 32K elements, a flat partition's norm pass cuts its whole
     gradient into at most 256 chunks of numel / 256 elements (a multiple of the update
-    chunk), whatever its segments, run as 1,024-thread blocks, and the update takes the
+    chunk), whatever its segments, run as 512-thread blocks, and the update takes the
     decisions itself.  With per-segment norms the chunks must follow the segments: fewer
     than 128 segments give chunks of numel / (256 - nseg) elements, more keep 32K-element
     chunks of 256-thread blocks and a finalize; so does the chunk-table update."""
@@ -247,13 +247,13 @@ def test_norm_pass_of_few_large_blocks(sizes):
     plan = Z.neox_zero1_plan(_cfg(), segs, tables=False)[0]
     C = plan.chunk_elems
     few = -(-(-(-n // 256)) // C) * C
-    assert plan.norm_chunk_elems == few and plan.norm_block_threads == 1024
+    assert plan.norm_chunk_elems == few and plan.norm_block_threads == 512
     assert plan.norm_chunks == -(-n // few) <= 256 and plan.update_decides == 1
     # per-segment norms
     plan = Z.neox_zero1_plan(_cfg(segment_norms=1), segs, tables=False)[0]
     few = -(-(-(-n // (256 - nseg))) // C) * C
     if nseg < 128 and few <= 1 << 28:
-        assert plan.norm_chunk_elems == few and plan.norm_block_threads == 1024
+        assert plan.norm_chunk_elems == few and plan.norm_block_threads == 512
         assert plan.norm_chunks <= 256 and plan.update_decides == 1
     else:
         assert plan.norm_chunk_elems == 32768 and plan.norm_block_threads == 256
