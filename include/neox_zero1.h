@@ -321,7 +321,9 @@ typedef struct neox_chunk_info {
 typedef struct neox_zero1_plan_t {
     uint64_t numel;                /* elements over all segments                        */
     uint64_t update_chunks;        /* entries of the update chunk table                 */
-    uint64_t norm_chunks;          /* entries of the norm pass's table                  */
+    uint64_t norm_chunks;          /* entries of the norm pass's table (on a flat       */
+                                   /*    partition without segment_norms they cut the  */
+                                   /*    whole gradient, across segment bounds)         */
     uint64_t flat_tiles;           /* tiles of the flat update; 0 on the chunked path   */
     uint64_t flat_changes;         /* in-tile decay-flag changes (flat path)            */
     uint32_t chunk_elems;          /* update chunk length                               */
