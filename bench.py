@@ -879,7 +879,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first (the first ~20 steps of a fresh process run up to 30%% slower while the GPU settles)")
     ap.add_argument("--workload", default="neox20b_shard_215m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cpu-large", action="store_true",
