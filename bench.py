@@ -872,7 +872,7 @@ def extra_workload(name, dev, steps, warmup):
 # the other shards of at least 2e8 params, timed in the default run: the largest one that
 # fits one GPU (OPT-style, 6e9 params, 96 GB of state) and the 5,000 separately allocated
 # tensors (chunk-table update)
-EXTRA_WORKLOADS = (("opt_style_6b", 6, 2), ("multi_tensor_5000_bf16", 20, 3))
+EXTRA_WORKLOADS = (("opt_style_6b", 6, 2), ("multi_tensor_5000_bf16", 20, 6))
 
 
 def main():
