@@ -100,6 +100,34 @@ MUTANTS = [
      "half[i] = orc_float_to_half(cfg->dtype, (float)(w1 * (1 + 1e-7)));", 1),
     ("overflow taken on the double product",
      "float g32 = (float)x * inv32;", "float g32 = (float)(x * inv);", 1),
+    ("growth past the FP32 range taken",
+     "if (!f32_nonfinite(s)) st->loss_scale = s;", "st->loss_scale = s;", 1),
+    ("clean-step counter kept after a growth",
+     "        if (!f32_nonfinite(s)) st->loss_scale = s;\n        st->good_steps = 0;\n",
+     "        if (!f32_nonfinite(s)) st->loss_scale = s;\n", 1),
+    ("skipped step advances t",
+     "        st->skipped_total += 1;\n", "        st->skipped_total += 1;\n        st->step += 1;\n", 1),
+    ("overflow run not accumulated",
+     "st->consecutive_overflows += 1;", "st->consecutive_overflows = 1;", 1),
+    ("second moment from the unclipped gradient",
+     "double v1 = b2 * v0 + (1.0 - b2) * (g * g);",
+     "double v1 = b2 * v0 + (1.0 - b2) * ((x * d->inv) * (x * d->inv));", 1),
+    ("decay on a half-updated weight",
+     "if (decay) u += wd * w0;\n        double w1 = w0 - rate * u;\n\n        float wf = (float)w1;\n"
+     "        exp_avg[i] = (float)m1;\n        exp_avg_sq",
+     "if (decay) u += wd * (w0 - rate * u);\n        double w1 = w0 - rate * u;\n\n"
+     "        float wf = (float)w1;\n        exp_avg[i] = (float)m1;\n        exp_avg_sq", 1),
+    ("norm of the FP32 unscaled value",
+     "double g = x * inv;\n        acc += g * g;", "double g = (double)g32;\n        acc += g * g;", 1),
+    ("bias correction in single precision",
+     "d->bc1 = 1.0 - pow(cfg->beta1, (double)t);",
+     "d->bc1 = 1.0 - (double)powf((float)cfg->beta1, (float)t);", 1),
+    ("scale floor test inverted",
+     "st->loss_scale = s < floor_ ? floor_ : s;", "st->loss_scale = s > floor_ ? floor_ : s;", 1),
+    ("truncating half cast",
+     "double k = nearbyint(ldexp(a, -q));", "double k = trunc(ldexp(a, -q));", 1),
+    ("eps added before the bias correction",
+     "double den = sqrt(v1 / d->bc2) + eps;", "double den = (sqrt(v1) + eps) / sqrt(d->bc2);", 1),
 ]
 
 PINS = [os.path.join(ROOT, "tests", f) for f in

@@ -228,7 +228,8 @@ def test_norm_exact_sum(dtype):
 
 def test_clip_norm_after_clip():
     """With clipping active the applied gradient has norm c: after step 1 from zero
-    moments, ||m1|| = (1 - beta1) * c."""
+    moments, ||m1|| = (1 - beta1) * c and sum(v1) = (1 - beta2) * c^2 (both moments see
+    the clipped gradient)."""
     n = 20_000
     rng = np.random.default_rng(13)
     for c in (1.0, 0.3):
@@ -240,6 +241,8 @@ def test_clip_norm_after_clip():
         assert st.last_norm > c
         m1 = math.sqrt(math.fsum(float(v) ** 2 for v in s["m"].astype(np.float64)))
         assert abs(m1 - (1 - cfg.beta1) * c) <= 1e-5 * (1 - cfg.beta1) * c
+        v1 = math.fsum(float(v) for v in s["v"].astype(np.float64))
+        assert abs(v1 - (1 - cfg.beta2) * c * c) <= 1e-5 * (1 - cfg.beta2) * c * c
         assert abs(st.last_coef * st.last_norm - c) <= 1e-12
 
 
