@@ -128,6 +128,19 @@ MUTANTS = [
      "double k = nearbyint(ldexp(a, -q));", "double k = trunc(ldexp(a, -q));", 1),
     ("eps added before the bias correction",
      "double den = sqrt(v1 / d->bc2) + eps;", "double den = (sqrt(v1) + eps) / sqrt(d->bc2);", 1),
+    ("padding decays",
+     "s->flags = (owner < ntensors && tensor_decay[owner]) ? ORC_DECAY : 0;",
+     "s->flags = (owner >= ntensors || tensor_decay[owner]) ? ORC_DECAY : 0;", 1),
+    ("rank of an element off by one",
+     "if (e / P != (uint64_t)rank) continue;", "if (e / (P + 1) != (uint64_t)rank) continue;", 1),
+    ("one tensor advanced per element",
+     "while (ti < ntensors && e >= tstart + tensor_numel[ti]) {",
+     "if (ti < ntensors && e >= tstart + tensor_numel[ti]) {", 1),
+    ("shard offset taken in the tensor",
+     "s->shard_offset = e - (uint64_t)rank * P;", "s->shard_offset = e - tstart;", 1),
+    ("padding given the last tensor's id",
+     "s->tensor_id = (uint32_t)owner;",
+     "s->tensor_id = (uint32_t)(owner < ntensors ? owner : ntensors - 1);", 1),
 ]
 
 PINS = [os.path.join(ROOT, "tests", f) for f in
