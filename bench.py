@@ -4,16 +4,24 @@
 One step = the whole hot path on the shard: norm/overflow pass, finalize, fused
 unscale + clip + AdamW + cast update.  Inputs are synthetic and already resident in
 HBM.  Prints one JSON line:
-  value     params/s over the timed steps (wall clock between synchronizations)
+  value     params/s over the timed steps (wall clock between synchronizations);
+            ms_per_step_median / ms_per_step_min from per-step dispatch events
+  hbm       the step's algorithmic bytes (30 B/param) and their rate against 8 TB/s
   roofline  the update kernel (the dominant one): algorithmic bytes per launch over its
-            average duration from HIP events its own dispatch stamps, against 8 TB/s;
+            average duration from HIP events its own dispatch stamps, against 8 TB/s,
+            and against a plain copy timed on the same GPU (frac_of_copy);
             traffic = HBM bytes per launch from the committed rocprofv3 counter summary
             of this workload and kernel (null when there is none for the current sources)
   kernel_avg_ms  norm / finalize / update durations (a short all-kernel pass after)
   skipped_step   the cost of a step with an inf in the gradient (timed last)
-  ceiling   a kernel with the update's access pattern and trivial arithmetic, swept over
-            launch shapes, and a plain copy, both on this GPU right after the timed steps
-  cpu_baseline  the CPU oracle, single thread, on a bounded sample of the workload
+  probes    a plain copy and a kernel with the update's access pattern and trivial
+            arithmetic, swept over launch shapes, on this GPU right after the timed steps
+  workloads the 6e9-parameter OPT-style shard and the 5,000-tensor layout, each with its
+            own timing, roofline and kernel split
+  cpu_baseline  the CPU oracle on the host's cores (all threads, static contiguous
+            pieces, per-thread double partials added in thread order) and on one thread,
+            on the whole shard; the smaller shards in full, the 5,000-tensor layout in
+            full and the 6e9 shard windowed; the host's CPU count, model and memory
 Other modes: --summarize-trace / --summarize-pmc write the profiles/ summaries from
 rocprofv3 output; --copy-probe-only is the counters' calibration copy.
 """
