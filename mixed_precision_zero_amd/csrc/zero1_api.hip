@@ -70,9 +70,20 @@ namespace {
 #ifndef NZ1_FLAT_BLOCKS_PER_CU
 #define NZ1_FLAT_BLOCKS_PER_CU 2
 #endif
-// momentum SGD moves 20 B/param over seven streams and prefers more blocks in flight
-#ifndef NZ1_FLAT_BLOCKS_PER_CU_SGD
-#define NZ1_FLAT_BLOCKS_PER_CU_SGD 4
+// Momentum SGD (20 B/param over seven streams, both update kernels): 4 blocks per CU
+// on grids of at most NZ1_SGD_SHORT_GRID blocks per CU, 2 on longer ones.  Measured on
+// MI355X, flat one-segment shards, same arrays, alternating builds, median us per
+// update at 4 / 2 blocks per CU: 2M elements 7.4 / 8.8, 8M 27.4 / 30.9, 16M 49.4 / 55.1,
+// 32M 103 / 112, 44M 157.5 / 150.2, 64M 230 / 218, 128M 460 / 427, the 215M shard
+// 756-760 / 707-710 (the grid has 61 blocks per CU at 32M and 84 at 44M).
+#ifndef NZ1_SGD_BLOCKS_PER_CU_SHORT
+#define NZ1_SGD_BLOCKS_PER_CU_SHORT 4
+#endif
+#ifndef NZ1_SGD_BLOCKS_PER_CU_LONG
+#define NZ1_SGD_BLOCKS_PER_CU_LONG 2
+#endif
+#ifndef NZ1_SGD_SHORT_GRID
+#define NZ1_SGD_SHORT_GRID 64
 #endif
 // Short update grids want more blocks in flight: a pass of a few blocks per CU is
 // dominated by its ramp-up and drain, while on long grids more tiles in flight mean more
@@ -591,10 +602,13 @@ int lds_reserve(int device, int optimizer, uint64_t update_blocks, LdsReserve* o
     out->norm_big = reserve_for(lds_per_cu, 1, norm_big_fixed);   // one large block per CU
     // the update kernels declare no static LDS
     if (optimizer == NEOX_OPT_SGD) {
-        // momentum SGD keeps its fixed shapes: 8 per CU measured slower at every size
-        // (16M elements 66.8 against 64.5 us at 4 per CU)
-        out->update = reserve_for(lds_per_cu, NZ1_UPDATE_BLOCKS_PER_CU, 0);
-        out->flat = reserve_for(lds_per_cu, NZ1_FLAT_BLOCKS_PER_CU_SGD, 0);
+        // momentum SGD never takes 8 per CU (measured slower at every size: 16M elements
+        // 66.8 against 64.5 us at 4 per CU)
+        const uint64_t per = (update_blocks + (uint64_t)cus - 1) / (uint64_t)cus;
+        const uint32_t sgd = per <= NZ1_SGD_SHORT_GRID ? NZ1_SGD_BLOCKS_PER_CU_SHORT
+                                                       : NZ1_SGD_BLOCKS_PER_CU_LONG;
+        out->update = reserve_for(lds_per_cu, sgd, 0);
+        out->flat = reserve_for(lds_per_cu, sgd, 0);
     } else {
         out->update = reserve_for(lds_per_cu, update_per_cu(update_blocks, cus, NZ1_UPDATE_BLOCKS_PER_CU), 0);
         out->flat = reserve_for(lds_per_cu, update_per_cu(update_blocks, cus, NZ1_FLAT_BLOCKS_PER_CU), 0);

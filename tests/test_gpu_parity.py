@@ -519,3 +519,36 @@ def test_launch_choice_boundaries(case):
     finally:
         chk.close()
     assert chk.ost.step == 2 and chk.ost.last_coef < 1.0
+
+
+# Momentum SGD runs 4 blocks per CU up to 64 grid blocks per CU and 2 beyond (on 256 CUs:
+# 16,384 tiles or chunks of 2,048 elements), in both update kernels.
+_SGD_BOUNDARY_SIZES = {
+    "grid_64_per_cu": 16384 * 2048,
+    "grid_64_per_cu_plus_ragged": 16384 * 2048 + 2048 + 3,
+}
+
+
+@pytest.mark.parametrize("chunked", [0, 1], ids=["flat", "chunk_table"])
+@pytest.mark.parametrize("case", sorted(_SGD_BOUNDARY_SIZES))
+def test_sgd_launch_choice_boundaries(case, chunked):
+    """Momentum SGD, every element against the oracle for two steps (the second with
+    clipping active) on either side of its blocks-per-CU boundary, in the flat and the
+    chunk-table update."""
+    n = _SGD_BOUNDARY_SIZES[case]
+    w = _custom(f"sgd_boundary_{case}", [n - 4099, 4099], [True, False], optimizer=1,
+                weight_decay=0.05, clip_norm=0.05)
+    shard = DeviceShard(w, flat=True)
+    plan = Z.neox_zero1_plan(lib_config(w, chunked_update=chunked), shard.neox_segments(),
+                             tables=False)[0]
+    assert plan.update_path == (Z.NEOX_PATH_CHUNKED if chunked else Z.NEOX_PATH_FLAT)
+    log(f"case sgd launch boundary {case} chunked={chunked}: {n} elements")
+    shard.init_()
+    chk = Checker(shard, chunked_update=chunked)
+    try:
+        for k in range(2):
+            shard.grads_(k, chk.scale())
+            chk.step(1e-2, threads=16, where=f" sgd {case} chunked={chunked} step {k}")
+    finally:
+        chk.close()
+    assert chk.ost.step == 2 and chk.ost.last_coef < 1.0
