@@ -87,19 +87,20 @@ namespace {
 #endif
 // Short update grids want more blocks in flight: a pass of a few blocks per CU is
 // dominated by its ramp-up and drain, while on long grids more tiles in flight mean more
-// open DRAM rows.  Up to NZ1_SMALL_GRID blocks per CU of grid the AdamW update runs 4
-// blocks per CU, up to NZ1_MID_GRID 8, beyond that the defaults above.  Measured on MI355X,
-// flat shards, us per step at 2 / 4 / 8 blocks per CU: 2M elements 18.5 / 15.9 / 15.9,
-// 8M 50.8 / 47.5 / 48.3, 16M 90.8 / 86.6 / 84.4, 20M 111.3 / 106.9 / 104.9, 24M
-// 125.7 / 127.4 / 125.4, 32M 171.5 / 180.1 / 185.1, 44M 239.7 / 246.3 / 255.0 (on 256
-// CUs the grid has 4 blocks per CU at 2M, 15 at 8M, 38 at 20M, 46 at 24M; M = 1e6
-// elements); the chunk-table update follows
-// the same curve (8M 66.3 / 53.0 / 52.8, 16M 95.8 / 91.4 / 91.5, 32M 177.5 / 181.0 / 187.5).
-#ifndef NZ1_SMALL_GRID
-#define NZ1_SMALL_GRID 16
-#endif
-#ifndef NZ1_MID_GRID
-#define NZ1_MID_GRID 40
+// open DRAM rows.  Up to NZ1_SHORT_GRID blocks per CU of grid the AdamW update runs 4
+// blocks per CU, beyond that the defaults above.  Measured on MI355X, one-segment shards,
+// same arrays, alternating builds, two rounds, median us per update at 2 / 4 / 8 blocks
+// per CU; flat (deciding) update: 4M 24.8-26.0 / 21.3-21.6 / 22.6-22.7, 8M 42.0-42.3 /
+// 37.1 / 39.3-39.4, 12M 60.8-62.0 / 54.7 / 55.4-56.0, 16M 77.6-77.8 / 71.5-71.6 /
+// 73.4-73.5, 20M 103.3-103.7 / 96.7-96.9 / 98.4-98.9, 24M 114.1-115.3 / 110.7-111.1 /
+// 112.1-112.2, 28M 135.3-135.8 / 143.2-143.8 / 143.6-143.7, 32M 155.3 / 165.7-166.4 /
+// 168.3-168.4, 44M 206.5-207.3 / 222.9-223.5 / 229.4-229.5; chunk-table update: 8M
+// 50.8-51.7 / 40.8-41.0 / 40.9-41.3, 16M 68.2-68.3 / 68.8-69.0 / 73.8-74.0, 24M
+// 115.5-115.7 / 107.7-108.0 / 107.2-107.4, 28M 141.8-142.5 / 139.7-140.5 / 141.8-142.1,
+// 32M 158.9-159.1 / 161.7-161.8 / 169.5-169.9 (on 256 CUs the grid has 15 blocks per CU
+// at 8M, 46 at 24M, 53 at 28M; M = 1e6 elements).
+#ifndef NZ1_SHORT_GRID
+#define NZ1_SHORT_GRID 48
 #endif
 // Timing events skip the system-scope fence an event otherwise performs when it
 // completes (an L2 write-back and invalidate that slows the kernels after it): they are
@@ -583,8 +584,7 @@ static uint32_t reserve_for(int lds_per_cu, uint32_t per_cu, uint32_t fixed) {
 // Blocks per CU for an update grid of `blocks` blocks on `cus` CUs.
 static uint32_t update_per_cu(uint64_t blocks, int cus, uint32_t long_grid) {
     const uint64_t per = (blocks + (uint64_t)cus - 1) / (uint64_t)cus;
-    if (per <= NZ1_SMALL_GRID) return long_grid > 4u ? long_grid : 4u;
-    if (per <= NZ1_MID_GRID) return long_grid > 8u ? long_grid : 8u;
+    if (per <= NZ1_SHORT_GRID) return long_grid > 4u ? long_grid : 4u;
     return long_grid;
 }
 

@@ -484,15 +484,15 @@ def test_norm_chunks_across_many_segments():
 
 
 # Shard sizes on either side of the library's size-dependent launch choices: the AdamW
-# update runs 4 blocks per CU up to 16 grid blocks per CU, 8 up to 40, else 2 (on 256 CUs:
-# 4,096 and 10,240 tiles of 2,048 elements), and the norm pass keeps the gradient cached
-# up to 2^24 elements.  Results must not depend on them.
+# update runs 4 blocks per CU up to 48 grid blocks per CU, else 2 (on 256 CUs: 12,288
+# tiles of 2,048 elements), and the norm pass keeps the gradient cached up to 2^24
+# elements.  Results must not depend on them.
 _BOUNDARY_SIZES = {
-    "grid_16_per_cu": (4096 * 2048, W.F16),
-    "grid_16_per_cu_plus_one_tile": (4096 * 2048 + 2048, W.F16),
+    "grid_48_per_cu": (12288 * 2048, W.F16),
+    "grid_48_per_cu_plus_one_tile": (12288 * 2048 + 2048, W.F16),
     "cached_norm_2e24": (1 << 24, W.F16),
     "uncached_norm_2e24_plus_ragged": ((1 << 24) + 2048 + 5, W.F16),
-    "grid_40_per_cu_plus_ragged": (10240 * 2048 + 3, W.F16),
+    "grid_48_per_cu_plus_ragged_bf16": (12288 * 2048 + 3, W.BF16),
     "large_norm_blocks_bf16": (3_000_007, W.BF16),
     "short_norm_chunks_2e6": (64 * 32767, W.F16),
 }
