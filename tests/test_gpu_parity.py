@@ -521,26 +521,63 @@ def test_launch_choice_boundaries(case):
     assert chk.ost.step == 2 and chk.ost.last_coef < 1.0
 
 
+# The chunk table of a two-segment shard (the second segment 4,099 elements) has 12,288
+# entries (48 per CU on 256 CUs) at the first size and 12,290 at the second.
+_TABLE_BOUNDARY_SIZES = {"table_48_per_cu": 12288 * 2048 - 2048,
+                         "table_49_per_cu": 12288 * 2048 + 2048}
+
+
+@pytest.mark.parametrize("case", sorted(_TABLE_BOUNDARY_SIZES))
+def test_launch_choice_boundaries_chunk_table(case):
+    """The same AdamW cut in the chunk-table update: every element against the oracle
+    for two steps (the second with clipping active) on either side of it."""
+    n, dtype = _TABLE_BOUNDARY_SIZES[case], W.F16
+    w = _custom(f"boundary_table_{case}", [n - 4099, 4099], [True, False], dtype=dtype,
+                clip_norm=0.05)
+    shard = DeviceShard(w, flat=True)
+    plan = Z.neox_zero1_plan(lib_config(w, chunked_update=1), shard.neox_segments(),
+                             tables=False)[0]
+    assert plan.update_path == Z.NEOX_PATH_CHUNKED
+    assert (plan.update_chunks <= 48 * 256) == (case == "table_48_per_cu"), plan.update_chunks
+    log(f"case launch boundary {case} on the chunk table: {n} elements, "
+        f"{plan.update_chunks} chunks")
+    shard.init_()
+    chk = Checker(shard, chunked_update=1)
+    try:
+        for k in range(2):
+            shard.grads_(k, chk.scale())
+            chk.step(w.hyper.lr, threads=16, where=f" {case} chunk table step {k}")
+    finally:
+        chk.close()
+    assert chk.ost.step == 2 and chk.ost.last_coef < 1.0
+
+
 # Momentum SGD runs 4 blocks per CU up to 64 grid blocks per CU and 2 beyond (on 256 CUs:
-# 16,384 tiles or chunks of 2,048 elements), in both update kernels.
+# 16,384 tiles or chunks of 2,048 elements), in both update kernels.  Sizes per kernel
+# (the chunk table also counts the second segment's head and tail chunks): the first of
+# each pair has a grid of 16,384 blocks, the second one of more.
 _SGD_BOUNDARY_SIZES = {
-    "grid_64_per_cu": 16384 * 2048,
-    "grid_64_per_cu_plus_ragged": 16384 * 2048 + 2048 + 3,
+    ("grid_64_per_cu", 0): 16384 * 2048,
+    ("grid_64_per_cu_plus_ragged", 0): 16384 * 2048 + 2048 + 3,
+    ("grid_64_per_cu", 1): 16384 * 2048 - 2048,
+    ("grid_64_per_cu_plus_ragged", 1): 16384 * 2048 + 2048 + 3,
 }
 
 
 @pytest.mark.parametrize("chunked", [0, 1], ids=["flat", "chunk_table"])
-@pytest.mark.parametrize("case", sorted(_SGD_BOUNDARY_SIZES))
+@pytest.mark.parametrize("case", ["grid_64_per_cu", "grid_64_per_cu_plus_ragged"])
 def test_sgd_launch_choice_boundaries(case, chunked):
     """Momentum SGD, every element against the oracle for two steps (the second with
     clipping active) on either side of its blocks-per-CU boundary, in the flat and the
     chunk-table update."""
-    n = _SGD_BOUNDARY_SIZES[case]
+    n = _SGD_BOUNDARY_SIZES[(case, chunked)]
     w = _custom(f"sgd_boundary_{case}", [n - 4099, 4099], [True, False], optimizer=1,
                 weight_decay=0.05, clip_norm=0.05)
     shard = DeviceShard(w, flat=True)
     plan = Z.neox_zero1_plan(lib_config(w, chunked_update=chunked), shard.neox_segments(),
                              tables=False)[0]
+    grid = plan.update_chunks if chunked else plan.flat_tiles
+    assert (grid <= 64 * 256) == (case == "grid_64_per_cu"), grid
     assert plan.update_path == (Z.NEOX_PATH_CHUNKED if chunked else Z.NEOX_PATH_FLAT)
     log(f"case sgd launch boundary {case} chunked={chunked}: {n} elements")
     shard.init_()
