@@ -247,10 +247,17 @@ int neox_zero1_destroy(neox_zero1* h);
  *   (caller)               gathers the D ranks' values, in rank order, into a device
  *                          array rank_sumsq[D] on every rank (an all-gather: data
  *                          movement only);
- *   neox_zero1_step_apply  enqueues the finalize -- which adds rank_sumsq[0 .. nranks) in
- *                          a fixed order, so every rank gets the same bits and takes the
- *                          same skip and clip decisions; a non-finite value from any rank
- *                          skips the step everywhere -- and the update.
+ *   neox_zero1_step_apply  adds rank_sumsq[0 .. nranks) in a fixed order, so every rank
+ *                          gets the same bits and takes the same skip and clip decisions
+ *                          (a non-finite value from any rank skips the step everywhere),
+ *                          and enqueues the update.  With at most 256 ranks on a handle
+ *                          whose update can decide (a flat partition, or a shard whose
+ *                          neox_zero1_step has no finalize launch) the update kernel adds
+ *                          the values and decides itself; otherwise a one-block finalize
+ *                          does it first.  The bits are the same either way.
+ * The step's scaler state is the one its step_local started from (the norm pass saves
+ * it): call neox_scaler_set between steps, not between a step_local and its step_apply,
+ * and give every step_apply its own step_local.
  * neox_zero1_step is step_local followed by step_apply on the local value alone
  * (nranks = 1), bit for bit.  Both return without waiting.  Errors: NEOX_EINVAL (null
  * handle or pointer, pointer not 8-byte aligned, nranks 0 or above 2^24, non-finite lr),

@@ -788,9 +788,12 @@ namespace nz1 {
 
 // norm pass (+ per-segment sums when enabled); snapshots the pre-step state for a fused
 // update
-static hipError_t enqueue_norm(const StepLaunch& s, hipStream_t stream, const KernelTiming& t) {
+// snap: the norm pass also copies the pre-step state to s.snap, for an update that takes
+// the step's decisions itself.
+static hipError_t enqueue_norm(const StepLaunch& s, bool snap, hipStream_t stream,
+                               const KernelTiming& t) {
     hipError_t e = launch_norm(s.dtype, s.norm_nt, s.norm_big, s.norm_chunks, s.nnorm,
-                               s.norm_blocks, s.st, s.partial, s.fused ? s.snap : nullptr,
+                               s.norm_blocks, s.st, s.partial, snap ? s.snap : nullptr,
                                s.norm_big ? s.lds.norm_big : s.lds.norm, stream, t);
     if (e == hipSuccess && s.seg_sumsq)
         e = launch_segment_sumsq(s.partial, s.seg_range, s.nseg, s.seg_sumsq, stream);
@@ -809,7 +812,7 @@ static hipError_t enqueue_update(const StepLaunch& s, float lr, const FuseIn* fu
 
 hipError_t enqueue_step(const StepLaunch& s, float lr, hipStream_t stream, const KernelTiming* t3) {
     const KernelTiming none{};
-    hipError_t e = enqueue_norm(s, stream, t3 ? t3[0] : none);
+    hipError_t e = enqueue_norm(s, s.fused, stream, t3 ? t3[0] : none);
     if (s.fused) {
         const FuseIn f{s.partial, s.norm_blocks, s.snap, s.st, s.fin};
         if (e == hipSuccess) e = enqueue_update(s, lr, &f, stream, t3 ? t3[2] : none);
@@ -818,6 +821,10 @@ hipError_t enqueue_step(const StepLaunch& s, float lr, hipStream_t stream, const
         if (e == hipSuccess) e = enqueue_update(s, lr, nullptr, stream, t3 ? t3[2] : none);
     }
     return e;
+}
+
+bool split_update_decides(const StepLaunch& s, uint32_t nranks) {
+    return kUpdateDecides && nranks <= kFuseMaxParts && (s.flat || s.fused);
 }
 
 hipError_t enqueue_update_only(const StepLaunch& s, float lr, hipStream_t stream) {
@@ -848,7 +855,7 @@ extern "C" int neox_zero1_step_local(neox_zero1* h, double* local_sumsq, void* h
     if (!h || !local_sumsq) return set_error(NEOX_EINVAL, "null argument");
     if ((uintptr_t)local_sumsq & 7u) return set_error(NEOX_EINVAL, "local_sumsq not 8-byte aligned");
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = enqueue_norm(h->sl, stream, KernelTiming{});
+    hipError_t e = enqueue_norm(h->sl, true, stream, KernelTiming{});
     if (e == hipSuccess) e = launch_reduce(h->sl.partial, h->sl.norm_blocks, local_sumsq, stream);
     h->last_stream = stream;
     if (e != hipSuccess) return set_hip_error(e, "step_local launch");
@@ -862,8 +869,16 @@ extern "C" int neox_zero1_step_apply(neox_zero1* h, const double* rank_sumsq, ui
     if ((uintptr_t)rank_sumsq & 7u) return set_error(NEOX_EINVAL, "rank_sumsq not 8-byte aligned");
     if (!std::isfinite(lr)) return set_error(NEOX_EINVAL, "lr %g is not finite", (double)lr);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = launch_finalize(rank_sumsq, nranks, h->sl.st, h->sl.fin, stream);
-    if (e == hipSuccess) e = enqueue_update_only(h->sl, lr, stream);
+    hipError_t e;
+    if (split_update_decides(h->sl, nranks)) {
+        // the update adds the ranks' values in the finalize's order and decides itself,
+        // from the pre-step state the norm pass of step_local saved
+        const FuseIn f{rank_sumsq, nranks, h->sl.snap, h->sl.st, h->sl.fin};
+        e = enqueue_update(h->sl, lr, &f, stream, KernelTiming{});
+    } else {
+        e = launch_finalize(rank_sumsq, nranks, h->sl.st, h->sl.fin, stream);
+        if (e == hipSuccess) e = enqueue_update_only(h->sl, lr, stream);
+    }
     h->last_stream = stream;
     if (e != hipSuccess) return set_hip_error(e, "step_apply launch");
     return NEOX_OK;

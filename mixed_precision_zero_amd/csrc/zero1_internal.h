@@ -274,5 +274,9 @@ struct StepLaunch {
 hipError_t enqueue_step(const StepLaunch& s, float lr, hipStream_t stream, const KernelTiming* t3);
 // the update alone after a finalize has taken the decision (split step)
 hipError_t enqueue_update_only(const StepLaunch& s, float lr, hipStream_t stream);
+// Whether the split step's update takes the decisions itself from nranks values: at most
+// kFuseMaxParts of them, and a layout whose update decides (a flat partition, or a norm
+// grid small enough that the single step's update decides too).
+bool split_update_decides(const StepLaunch& s, uint32_t nranks);
 
 }  // namespace nz1

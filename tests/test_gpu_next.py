@@ -32,9 +32,9 @@ def _outputs(shard):
 def test_split_step_equals_step_on_one_rank(sizes):
     """step == step_local followed by step_apply on the local value, bit for bit.  With
     per-segment norms the norm chunks follow the segments, so these shards' norm passes
-    have from 38 up to 256 blocks; the step's update takes the decisions itself while the
-    split step's finalize takes them: the two must agree bit for bit, whether the
-    partials fill one wave of the finalize or all four."""
+    have from 38 up to 256 blocks, whose partials fill one wave of the fixed-order sum or
+    all four; the step's update adds the partials itself, the split step reduces them to
+    one value first, and the two must agree bit for bit."""
     w = _custom("split1", sizes, [k % 3 != 1 for k in range(len(sizes))], clip_norm=0.05)
     w.injections = {2: [(10, "nan")]}
     stream = torch.cuda.current_stream().cuda_stream
@@ -108,6 +108,50 @@ def test_split_step_with_telemetry_and_sgd(optimizer):
     assert seq_a[1][0][2] == 1                                # that step was skipped
     for k in out_a:
         assert torch.equal(out_a[k], out_b[k]), k
+
+
+@pytest.mark.parametrize("optimizer", [Z.NEOX_OPT_ADAMW, Z.NEOX_OPT_SGD], ids=["adamw", "sgd"])
+def test_split_apply_update_decides_like_the_finalize(optimizer):
+    """step_apply over at most 256 rank values lets the update add them and decide; over
+    more it launches the finalize.  The sum of 256 values and of the same values followed
+    by one +0.0 have the same bits in the fixed order, so the two paths, on identical
+    shards, must give identical outputs and scaler state every step: clipping active, a
+    NaN on one rank skipping a step, the local value at rank 5 of 256."""
+    w = _custom("split_paths", [300_000, 4099, 65_536], [True, False, True], clip_norm=0.05,
+                optimizer=optimizer)
+    w.injections = {2: [(123, "nan")]}
+    stream = torch.cuda.current_stream().cuda_stream
+    shards = [DeviceShard(w), DeviceShard(w)]
+    hs = []
+    for sh in shards:
+        sh.init_()
+        hs.append(Z.neox_zero1_create(lib_config(w), sh.neox_segments(), stream))
+    rng = np.random.default_rng(77)
+    others = torch.tensor(rng.uniform(0.5, 2.0, 256), dtype=torch.float64, device="cuda")
+    loc = torch.zeros(1, dtype=torch.float64, device="cuda")
+    try:
+        for k in range(4):
+            ranks = []
+            for sh, h, n in zip(shards, hs, (256, 257)):
+                sh.grads_(k, Z.neox_scaler_state(h).loss_scale)
+                Z.neox_zero1_step_local(h, loc.data_ptr(), stream)
+                r = torch.zeros(n, dtype=torch.float64, device="cuda")
+                r[:256] = others * loc        # the other ranks: multiples of this one
+                r[5] = loc[0]
+                Z.neox_zero1_step_apply(h, r.data_ptr(), 1e-3, stream, nranks=n)
+                ranks.append(r)
+            a, b = (Z.neox_scaler_state(h) for h in hs)
+            assert (a.loss_scale, a.step, a.skipped_total, a.last_sumsq, a.last_clip_coef) == \
+                (b.loss_scale, b.step, b.skipped_total, b.last_sumsq, b.last_clip_coef), k
+            if k != 2:
+                assert a.last_clip_coef < 1.0 and not a.last_skipped
+            oa, ob = _outputs(shards[0]), _outputs(shards[1])
+            for name in oa:
+                assert torch.equal(oa[name], ob[name]), (k, name)
+        assert Z.neox_scaler_state(hs[0]).skipped_total == 1
+    finally:
+        for h in hs:
+            Z.neox_zero1_destroy(h)
 
 
 @pytest.mark.parametrize("D", [4, 8])
