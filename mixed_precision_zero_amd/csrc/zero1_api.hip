@@ -786,10 +786,8 @@ extern "C" int neox_zero1_create(const neox_zero1_config* cfg, const neox_segmen
 
 namespace nz1 {
 
-// norm pass (+ per-segment sums when enabled); snapshots the pre-step state for a fused
-// update
-// snap: the norm pass also copies the pre-step state to s.snap, for an update that takes
-// the step's decisions itself.
+// norm pass (+ per-segment sums when enabled); with snap it also copies the pre-step
+// state to s.snap, for an update that takes the step's decisions itself
 static hipError_t enqueue_norm(const StepLaunch& s, bool snap, hipStream_t stream,
                                const KernelTiming& t) {
     hipError_t e = launch_norm(s.dtype, s.norm_nt, s.norm_big, s.norm_chunks, s.nnorm,
