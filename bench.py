@@ -13,6 +13,8 @@ HBM.  Prints one JSON line:
             traffic = HBM bytes per launch from the committed rocprofv3 counter summary
             of this workload and kernel (null when there is none for the current sources)
   kernel_avg_ms  norm / finalize / update durations (a short all-kernel pass after)
+  split_step     the step a data-parallel rank runs (step_local, step_apply over 96
+                 ranks' values; the exchange between them is not timed)
   skipped_step   the cost of a step with an inf in the gradient (timed last)
   probes    a plain copy and a kernel with the update's access pattern and trivial
             arithmetic, swept over launch shapes, on this GPU right after the timed steps
@@ -730,6 +732,43 @@ def time_skipped_steps(Z, h, grad, one_step, steps, events):
     return ms, kernels
 
 
+# Data-parallel ranks of the GPT-NeoX-20B run that the 215M shard is one of (20.6e9 / 96).
+SPLIT_RANKS = 96
+
+
+def time_split_steps(Z, h, lr, stream, steps, ranks=SPLIT_RANKS, rank=0, device="cuda"):
+    """The step a data-parallel rank runs: step_local, the exchange of the ranks' squared
+    norms, step_apply over all `ranks` values.  The exchange itself needs other GPUs and
+    is left out: step_local writes the local value straight into its slot of the rank
+    array, and the other ranks' slots hold fixed values near it.  Returns wall ms per
+    step over `steps` steps after 3 untimed ones; asserts that none was skipped."""
+    import torch
+
+    r = torch.zeros(ranks, dtype=torch.float64, device=device)
+    slot = r.data_ptr() + 8 * rank
+
+    def one():
+        Z.neox_zero1_step_local(h, slot, stream)
+        Z.neox_zero1_step_apply(h, r.data_ptr(), lr, stream, nranks=ranks)
+
+    Z.neox_zero1_step_local(h, slot, stream)
+    torch.cuda.synchronize()
+    local = float(r[rank])
+    others = torch.linspace(0.9, 1.1, ranks, dtype=torch.float64, device=device) * local
+    r.copy_(others)
+    before = Z.neox_scaler_state(h).skipped_total
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    assert Z.neox_scaler_state(h).skipped_total == before, "split steps were skipped"
+    return ms
+
+
 def alloc_shard(w, dev, sgd):
     """The workload's five device arrays (one buffer per array for a flat shard, else one
     allocation per array per segment), initialized, with the step-0 gradient drawn; the
@@ -1006,6 +1045,11 @@ def main():
     st = Z.neox_scaler_state(h)
     done = args.warmup + args.steps * (2 if timed_events else 1)
     assert st.skipped_total == 0 and st.step == done, "bench steps were skipped"
+    split = None
+    if not args.split and not args.graph and not args.segment_norms:
+        print(f"[bench] {args.steps} split steps over {SPLIT_RANKS} ranks", file=sys.stderr,
+              flush=True)
+        split = time_split_steps(Z, h, w.hyper.lr, stream.cuda_stream, args.steps)
     skipped = None
     if args.skip_steps > 0:
         print(f"[bench] {args.skip_steps} skipped steps (inf in the gradient)", file=sys.stderr,
@@ -1065,6 +1109,12 @@ def main():
                            "bytes_per_launch": upd_bpp * n}
         out["kernel_avg_ms"] = {"norm": t["norm_ms"], "finalize": t["finalize_ms"],
                                 "update": t["update_ms"]}
+    if split:
+        out["split_step"] = {"ranks": SPLIT_RANKS, "steps": args.steps, "ms_per_step": split,
+                             "value": n / (split * 1e-3), "unit": "params/s",
+                             "note": "step_local + step_apply over the ranks' squared norms, "
+                                     "the step a data-parallel rank runs; the exchange "
+                                     "between them needs other GPUs and is not timed"}
     if skipped:
         sk_ms, sk_kernels = skipped
         out["skipped_step"] = {"steps": args.skip_steps, "ms_per_step": sk_ms,

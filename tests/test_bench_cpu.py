@@ -203,6 +203,57 @@ def test_skipped_step_timing_restores_the_gradient(monkeypatch):
         bench.time_skipped_steps(lib, 0, grad, make_step(lib), 3, events=False)
 
 
+def test_split_step_timing_writes_the_local_slot(monkeypatch):
+    """bench.time_split_steps: step_local writes into the rank array at the rank's slot,
+    step_apply gets the whole array and the rank count every step, the other slots are
+    filled once, and a skipped split step is refused.  A fake library stands in for the
+    GPU here."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+
+    class FakeLib:
+        def __init__(self, skip):
+            self.calls, self.skip, self.skipped = [], skip, 0
+
+        def neox_zero1_step_local(self, h, ptr, stream):
+            self.calls.append(("local", ptr))
+            self.local_ptr = ptr
+            # the library writes 2.0 at ptr
+            self.array.view(-1)[(ptr - self.array.data_ptr()) // 8] = 2.0
+
+        def neox_zero1_step_apply(self, h, ptr, lr, stream, nranks):
+            self.calls.append(("apply", ptr, nranks))
+            if self.skip:
+                self.skipped += 1
+
+        def neox_scaler_state(self, h):
+            class S:
+                pass
+            st = S()
+            st.skipped_total = self.skipped
+            return st
+
+    real_zeros = torch.zeros
+
+    def zeros(*a, **k):
+        t = real_zeros(*a, **k)
+        lib.array = t
+        return t
+
+    monkeypatch.setattr(torch, "zeros", zeros)
+    lib = FakeLib(skip=False)
+    ms = bench.time_split_steps(lib, 0, 1e-3, 0, 4, ranks=8, rank=3, device="cpu")
+    assert ms >= 0.0
+    base = lib.array.data_ptr()
+    assert lib.calls[0] == ("local", base + 24)
+    assert lib.calls[1:] == [("local", base + 24), ("apply", base, 8)] * 7
+    assert float(lib.array[3]) == 2.0
+    assert torch.allclose(lib.array[[0, 7]], torch.tensor([1.8, 2.2], dtype=torch.float64))
+    lib = FakeLib(skip=True)
+    with pytest.raises(AssertionError):
+        bench.time_split_steps(lib, 0, 1e-3, 0, 2, ranks=4, rank=0, device="cpu")
+
+
 def test_stall_summary_table(tmp_path):
     """bench.summarize_stalls: per-kernel averages of the memory-side counters, turned into
     the duration, effective clock, latencies (LEVEL / REQ), requests in flight (LEVEL /
