@@ -497,7 +497,7 @@ def _time_oracle(cfg, st, segs, n, threads, budget_s, max_steps):
 def cpu_baseline(w, budget_s=10.0, dev=None):
     """The CPU oracle on this host: the bench workload in full, on all the cores this
     process may use (up to the box's share) and on one thread, plus the two small
-    workloads on all cores; with dev, also the two large workloads (the 5,000-tensor
+    workloads on all cores and on one thread; with dev, also the two large workloads (the 5,000-tensor
     shard in full, the 6e9 shard windowed), their inputs drawn on that device.  Inputs
     follow each workload's recipe (seeded host draws unless stated)."""
     info = host_info()
@@ -512,8 +512,11 @@ def cpu_baseline(w, budget_s=10.0, dev=None):
         sw = make_workload(name, partition="oracle")
         c, s2, sg, k = _oracle_setup(sw)
         r, ns, sec = _time_oracle(c, s2, sg, k, threads, 1.0, 20)
+        r1, ns1, sec1 = _time_oracle(c, s2, sg, k, 1, 1.0, 20)
         small[name] = {"value": r, "params": k, "steps": ns, "seconds": round(sec, 2),
-                       "cores": threads}
+                       "cores": threads,
+                       "single_thread": {"value": r1, "steps": ns1, "seconds": round(sec1, 2),
+                                         "cores": 1}}
     large = {}
     if dev is not None:
         for name, fn in (("multi_tensor_5000_bf16", cpu_multi_tensor_in_full),
