@@ -71,7 +71,8 @@ static_assert(offsetof(DevState, skip) % 16 == 0, "update fields share one 16-by
 // best on MI355X: 128 threads x 2 vectors (2,048-element tiles) at 2 blocks per CU on
 // long grids; fewer tiles in flight per CU keep the chip's open DRAM rows few, and the
 // block's single round trip keeps that low occupancy from exposing latency.  (Grids of
-// up to 40 blocks per CU run 4 or 8 blocks per CU instead; see lds_reserve.)
+// up to 48 blocks per CU, 64 for momentum SGD, run 4 blocks per CU instead; see
+// lds_reserve.)
 #ifndef NZ1_FLAT_BLOCK
 #define NZ1_FLAT_BLOCK 128
 #endif
