@@ -110,6 +110,49 @@ def test_split_step_with_telemetry_and_sgd(optimizer):
         assert torch.equal(out_a[k], out_b[k]), k
 
 
+def test_split_step_keeps_the_finalize_on_a_large_chunk_table():
+    """A separately allocated shard of ~9M elements: its norm pass has more than 256
+    blocks, so neither its step's update nor its split step's update decides; both run
+    the finalize, and step == step_local + step_apply (one rank) bit for bit, with
+    clipping active and a skipped step."""
+    w = _custom("split_table", [4_000_000, 3_000_001, 2_000_000, 77], [True, False, True, False],
+                clip_norm=0.05)
+    w.flat = False
+    w.injections = {1: [(3_999_999, "-inf")]}
+    stream = torch.cuda.current_stream().cuda_stream
+    outs, states = [], []
+    for mode in ("step", "split"):
+        sh = DeviceShard(w)
+        sh.init_()
+        cfg = lib_config(w)
+        plan = Z.neox_zero1_plan(cfg, sh.neox_segments(), tables=False)[0]
+        assert plan.update_path == Z.NEOX_PATH_CHUNKED and plan.update_decides == 0
+        assert plan.norm_chunks > 256, plan.norm_chunks
+        h = Z.neox_zero1_create(cfg, sh.neox_segments(), stream)
+        loc = torch.zeros(1, dtype=torch.float64, device="cuda")
+        seq = []
+        try:
+            for k in range(3):
+                sh.grads_(k, Z.neox_scaler_state(h).loss_scale)
+                if mode == "step":
+                    Z.neox_zero1_step(h, 1e-3, stream)
+                else:
+                    Z.neox_zero1_step_local(h, loc.data_ptr(), stream)
+                    Z.neox_zero1_step_apply(h, loc.data_ptr(), 1e-3, stream)
+                st = Z.neox_scaler_state(h)
+                seq.append((st.loss_scale, st.step, st.skipped_total, st.last_sumsq,
+                            st.last_clip_coef))
+        finally:
+            Z.neox_zero1_destroy(h)
+        log(f"case split on a large chunk table mode={mode}")
+        outs.append(_outputs(sh))
+        states.append(seq)
+    assert states[0] == states[1]
+    assert states[0][1][2] == 1 and states[0][2][4] < 1.0
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+
+
 @pytest.mark.parametrize("optimizer", [Z.NEOX_OPT_ADAMW, Z.NEOX_OPT_SGD], ids=["adamw", "sgd"])
 def test_split_apply_update_decides_like_the_finalize(optimizer):
     """step_apply over at most 256 rank values lets the update add them and decide; over
