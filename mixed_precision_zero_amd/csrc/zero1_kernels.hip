@@ -91,11 +91,21 @@ struct Fmt<2> {
 #define NZ1_NORM_UNROLL 8
 #endif
 constexpr int kNormUnroll = NZ1_NORM_UNROLL;   // 16-byte loads in flight per norm thread
-#ifndef NZ1_UPDATE_NT_LOAD
-#define NZ1_UPDATE_NT_LOAD 0
+// The update reads the gradient with non-temporal loads (it is read once and not written)
+// and the FP32 state, which it writes back in place, with ordinary ones.  Measured on
+// MI355X, same arrays, alternating builds, median us per update, ordinary / non-temporal
+// gradient loads: 215M shard 992-1017 / 985-994 (momentum SGD 704-722 / 695-700, chunk
+// table 1070-1077 / 1060-1063), a Pythia-410M rank 214 / 208-209, the 5,000-tensor
+// layout 5059-5077 / 5012-5021, the 6e9 shard 29.05-29.07 / 28.06-28.08 ms;
+// non-temporal loads of the state too: 215M 1182-1188.
+#ifndef NZ1_UPDATE_NT_GRAD
+#define NZ1_UPDATE_NT_GRAD 1
+#endif
+#ifndef NZ1_UPDATE_NT_STATE
+#define NZ1_UPDATE_NT_STATE 0
 #endif
 // Non-temporal stores of the update's results: measured 1-2% faster at the update's low
-// occupancy (they were neutral at full occupancy); non-temporal loads are ~10% slower.
+// occupancy (they were neutral at full occupancy).
 #ifndef NZ1_UPDATE_NT_STORE
 #define NZ1_UPDATE_NT_STORE 1
 #endif
@@ -611,8 +621,8 @@ __device__ __forceinline__ void load8(const uint4* __restrict__ g4, const float4
                                       const float4* __restrict__ m4, const float4* __restrict__ v4,
                                       uint64_t i, uint4& G, float4 (&W)[2], float4 (&M)[2],
                                       float4 (&V)[2]) {
-    constexpr bool NTL = NZ1_UPDATE_NT_LOAD;
-    G = ld16<NTL>(g4 + i);
+    constexpr bool NTG = NZ1_UPDATE_NT_GRAD, NTL = NZ1_UPDATE_NT_STATE;
+    G = ld16<NTG>(g4 + i);
     W[0] = ld16<NTL>(w4 + 2 * i);
     W[1] = ld16<NTL>(w4 + 2 * i + 1);
     M[0] = ld16<NTL>(m4 + 2 * i);
